@@ -1,0 +1,204 @@
+"""CPU oracle for the m=1 decode matvec path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  The HIP library never imports, links or calls it, and it never calls
+the HIP library: the two share no code.  Inputs come from ``synth`` (seeded generators only).
+
+What it computes (docs.rs pages of memra-engine 0.125.0):
+
+* RMSNorm, from the fused-producer gate page (src/bin/q8_fuse_gate.rs, module doc and
+  ``run_shape``): per row z = x * w / sqrt(mean(x^2) + eps), eps = 1e-6 given as an f32.
+  Here, in f64: ss = the exactly rounded sum of x_j^2 (``math.fsum``; each square is exact in
+  f64), s = 1 / sqrt(ss / ncols + eps), z64_j = (x_j * w_j) * s (x_j * w_j is exact in f64).
+  The f32 output the producer stores is z32 = float32(z64).
+* q8_1 quantisation (same page: int8 qs plus one f32 scale per 32 values, ``id = 1/d``),
+  in f32 -- see ``oracle.c``.
+* The three GEMVs of the bench page (src/bin/gemv_e4m3_bench.rs, module doc THE COMPARISON
+  and THE BLOCK-128 ARM), f64 terms and sums -- see ``oracle.c``.
+
+Readings where the pages are silent are listed in the repository's design notes; the ones that
+decide a value are restated next to the function that takes them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+EPS = 1e-6
+
+
+def build() -> None:
+    """Compile ``oracle.c`` (plain C, IEEE, no contraction) into ``liboracle.so``."""
+    src = os.path.join(_HERE, "oracle.c")
+    tmp = _SO + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
+                           "-fPIC", "-shared", src, "-o", tmp, "-lm"])
+    os.replace(tmp, _SO)
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_fp16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_fp16_value.restype = ctypes.c_double
+        lib.oracle_quantize_q8_1.argtypes = [vp, i32, i32, vp, vp]
+        lib.oracle_quantize_q8_1.restype = i32
+        lib.oracle_gemv_q8_0.argtypes = [vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+        lib.oracle_gemv_q8_0.restype = i32
+        lib.oracle_gemv_e4m3.argtypes = [vp, i64, f32, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+        lib.oracle_gemv_e4m3.restype = i32
+        lib.oracle_gemv_e4m3_blk128.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, i32, i32,
+                                                i32, vp, vp]
+        lib.oracle_gemv_e4m3_blk128.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------------- decoders
+
+def e4m3_value(code: int) -> float:
+    """OCP E4M3 value of one byte (NaN for 0x7F / 0xFF)."""
+    return _load().oracle_e4m3_value(code)
+
+
+def fp16_value(bits: int) -> float:
+    """IEEE binary16 value of one bit pattern."""
+    return _load().oracle_fp16_value(bits)
+
+
+# ------------------------------------------------------------------------- producer
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float = EPS):
+    """RMSNorm of f32 rows x [nrows, ncols] with gain w [ncols].
+
+    Returns (z64, z32, s64): the f64 result, its f32 rounding and the per-row f64 factor
+    s = 1 / sqrt(mean(x^2) + eps).  eps is taken as an f32 constant (1e-6f), as the gate
+    page passes it, then widened to f64.
+    """
+    x = np.atleast_2d(_c(x, np.float32))
+    w = _c(w, np.float32)
+    nrows, ncols = x.shape
+    assert w.shape == (ncols,)
+    eps64 = float(np.float32(eps))
+    x64 = x.astype(np.float64)
+    w64 = w.astype(np.float64)
+    z64 = np.empty((nrows, ncols), dtype=np.float64)
+    s64 = np.empty(nrows, dtype=np.float64)
+    for r in range(nrows):
+        ss = math.fsum(x64[r] * x64[r])
+        s = 1.0 / math.sqrt(ss / ncols + eps64)
+        s64[r] = s
+        z64[r] = (x64[r] * w64) * s
+    return z64, z64.astype(np.float32), s64
+
+
+def quantize_q8_1(z: np.ndarray):
+    """q8_1 of f32 rows z [nrows, ncols]: (qs int8 [nrows, ncols], d f32 [nrows, ncols/32])."""
+    z = np.atleast_2d(_c(z, np.float32))
+    nrows, ncols = z.shape
+    qs = np.empty((nrows, ncols), dtype=np.int8)
+    d = np.empty((nrows, ncols // 32), dtype=np.float32)
+    rc = _load().oracle_quantize_q8_1(z.ctypes.data, nrows, ncols, qs.ctypes.data, d.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_q8_1: bad shape ({rc})")
+    return qs, d
+
+
+def rmsnorm_q8_1(x: np.ndarray, w: np.ndarray, eps: float = EPS):
+    """The producer: RMSNorm then q8_1 of its f32 output.
+
+    Returns dict with z64, z32, qs, d and d64 = max|z64| / 127 per block (for tolerances).
+    """
+    z64, z32, s64 = rms_norm(x, w, eps)
+    qs, d = quantize_q8_1(z32)
+    nrows, ncols = z64.shape
+    d64 = np.abs(z64).reshape(nrows, ncols // 32, 32).max(axis=2) / 127.0
+    return {"z64": z64, "z32": z32, "s64": s64, "qs": qs, "d": d, "d64": d64}
+
+
+# --------------------------------------------------------------------------- GEMVs
+
+def _gemv_out(m, out_f):
+    y = np.full((m, out_f), np.nan, dtype=np.float64)
+    A = np.full((m, out_f), np.nan, dtype=np.float64)
+    return y, A
+
+
+def _rows(rows, out_f):
+    if rows is None:
+        return 0, out_f
+    r0, r1 = rows
+    return int(r0), int(r1)
+
+
+def _act(qs, d, in_f):
+    qs = np.atleast_2d(_c(qs, np.int8))
+    d = np.atleast_2d(_c(d, np.float32))
+    m = qs.shape[0]
+    assert qs.shape == (m, in_f) and d.shape == (m, in_f // 32)
+    return qs, d, m
+
+
+def gemv_q8_0(W, row_bytes, qs, d, in_f, out_f, rows=None):
+    """Q8_0 GEMV. Returns (y, A), f64 [m, out_f]; rows outside ``rows`` are NaN."""
+    W = _c(W, np.uint8)
+    qs, d, m = _act(qs, d, in_f)
+    assert W.size >= out_f * row_bytes
+    y, A = _gemv_out(m, out_f)
+    r0, r1 = _rows(rows, out_f)
+    rc = _load().oracle_gemv_q8_0(W.ctypes.data, row_bytes, qs.ctypes.data, d.ctypes.data, m,
+                                  in_f, out_f, r0, r1, y.ctypes.data, A.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_gemv_q8_0 refused its input ({rc})")
+    return y, A
+
+
+def gemv_e4m3(W, row_bytes, scale, qs, d, in_f, out_f, rows=None):
+    """Per-tensor-scale e4m3 GEMV. Returns (y, A), f64 [m, out_f]."""
+    W = _c(W, np.uint8)
+    qs, d, m = _act(qs, d, in_f)
+    assert W.size >= out_f * row_bytes
+    y, A = _gemv_out(m, out_f)
+    r0, r1 = _rows(rows, out_f)
+    rc = _load().oracle_gemv_e4m3(W.ctypes.data, row_bytes, float(scale), qs.ctypes.data,
+                                  d.ctypes.data, m, in_f, out_f, r0, r1, y.ctypes.data,
+                                  A.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_gemv_e4m3 refused its input ({rc})")
+    return y, A
+
+
+def gemv_e4m3_blk128(W, row_bytes, grid, qs, d, in_f, out_f, rows=None):
+    """Block-128-scaled e4m3 GEMV. Returns (y, A), f64 [m, out_f]."""
+    W = _c(W, np.uint8)
+    grid = _c(grid, np.float32)
+    qs, d, m = _act(qs, d, in_f)
+    grid_cols = (in_f + 127) // 128
+    assert W.size >= out_f * row_bytes and grid.size == ((out_f + 127) // 128) * grid_cols
+    y, A = _gemv_out(m, out_f)
+    r0, r1 = _rows(rows, out_f)
+    rc = _load().oracle_gemv_e4m3_blk128(W.ctypes.data, row_bytes, grid.ctypes.data, grid_cols,
+                                         qs.ctypes.data, d.ctypes.data, m, in_f, out_f, r0, r1,
+                                         y.ctypes.data, A.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_gemv_e4m3_blk128 refused its input ({rc})")
+    return y, A

@@ -1,0 +1,324 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the oracle itself.
+
+Each test ties one oracle function to something independent of it: values the pages print
+(golden fixtures, each with its citation), a library routine that implements the same
+definition (torch's float8_e4m3fn cast, numpy's float16, torch's rms_norm, numpy matmul),
+exact rational brute force on tiny inputs, closed forms and invariants.  The cases are
+chosen so that a plausible slip (a dropped term, a wrong sign or index, a transposed
+operand, the wrong rounding rule) fails at least one of them.
+"""
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from golden_io import read_blocks, read_points
+
+
+# ----------------------------------------------------------------------------- decoders
+
+def _same(a: float, b: float) -> bool:
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
+    return a == b and math.copysign(1.0, a) == math.copysign(1.0, b)
+
+
+def test_e4m3_golden_points():
+    pts = read_points("e4m3_points.txt")
+    assert len(pts) >= 10
+    for code, want in pts:
+        assert _same(oracle.e4m3_value(code), want), hex(code)
+
+
+def test_e4m3_exhaustive_against_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        assert _same(oracle.e4m3_value(c), float(lib[c])), hex(c)
+
+
+def test_fp16_golden_points():
+    pts = read_points("fp16_points.txt")
+    for bits, want in pts:
+        assert _same(oracle.fp16_value(bits), want), hex(bits)
+
+
+def test_fp16_exhaustive_against_numpy():
+    bits = np.arange(65536, dtype=np.uint16)
+    lib = bits.view(np.float16).astype(np.float64)
+    for b in range(65536):
+        assert _same(oracle.fp16_value(b), float(lib[b])), hex(b)
+
+
+# ---------------------------------------------------------------------------- quantiser
+
+def test_q8_1_golden_blocks():
+    blocks = read_blocks("q8_1_blocks.txt")
+    assert {"unit_scale_ties", "pow2_scaled", "all_zero", "constant", "negative_max",
+            "reciprocal_not_division"} <= set(blocks)
+    for name, blk in blocks.items():
+        z = np.array(blk["z"], dtype=np.float32)
+        assert z.shape == (32,) and np.all(z.astype(np.float64) == np.array(blk["z"])), name
+        qs, d = oracle.quantize_q8_1(z[None, :])
+        assert qs[0].tolist() == blk["q"], name
+        if "d" in blk:
+            assert float(d[0, 0]) == blk["d"], name
+
+
+def _blocks(seed, nblocks):
+    return synth.f32(seed, nblocks * 32).reshape(nblocks, 32)
+
+
+def test_q8_1_scale_is_correctly_rounded_amax_over_127():
+    z = _blocks(11, 2000)
+    qs, d = oracle.quantize_q8_1(z.reshape(1, -1))
+    d = d.reshape(-1)
+    amax = np.abs(z).max(axis=1)
+    for i in range(0, 2000, 7):
+        exact = Fraction(float(amax[i])) / 127
+        got = Fraction(float(d[i]))
+        for nb in (np.nextafter(d[i], np.float32(np.inf)), np.nextafter(d[i], np.float32(0))):
+            assert abs(got - exact) <= abs(Fraction(float(nb)) - exact)
+
+
+def test_q8_1_invariants():
+    z = _blocks(12, 4000)
+    # make some blocks small, some spread over binades, one negative-dominant
+    z[::3] *= np.float32(2.0 ** -12)
+    z[1::5, 7] = np.float32(-9.5)
+    qs, d = oracle.quantize_q8_1(z.reshape(1, -1))
+    qs = qs.reshape(-1, 32).astype(np.int64)
+    d = d.reshape(-1).astype(np.float64)
+    z64 = z.astype(np.float64)
+    assert np.all(np.abs(qs) <= 127)
+    arg = np.abs(z).argmax(axis=1)
+    rows = np.arange(len(z))
+    assert np.all(qs[rows, arg] == np.sign(z64[rows, arg]) * 127)
+    # q is z/d to the nearest integer (the f32 product z * (1/d) is within a few ulps of z/d)
+    err = np.abs(z64 / d[:, None] - qs)
+    assert err.max() <= 0.5 + 1e-4
+    # a sign is never flipped
+    assert np.all(qs * np.sign(z64) >= 0)
+    # rows of a 2-D call are independent
+    z2 = z[:64].reshape(2, 1024)
+    q2, d2 = oracle.quantize_q8_1(z2)
+    for r in range(2):
+        qr, dr = oracle.quantize_q8_1(z2[r:r + 1])
+        assert np.array_equal(q2[r], qr[0]) and np.array_equal(d2[r], dr[0])
+
+
+@pytest.mark.parametrize("k", [-20, -7, -1, 1, 5, 30])
+def test_q8_1_power_of_two_scaling(k):
+    z = _blocks(13, 500)
+    q0, d0 = oracle.quantize_q8_1(z.reshape(1, -1))
+    zs = (z.astype(np.float64) * 2.0 ** k).astype(np.float32)
+    q1, d1 = oracle.quantize_q8_1(zs.reshape(1, -1))
+    assert np.array_equal(q0, q1)
+    assert np.array_equal(d1.astype(np.float64), d0.astype(np.float64) * 2.0 ** k)
+
+
+# ------------------------------------------------------------------------------ RMSNorm
+
+EPS32 = float(np.float32(1e-6))
+
+
+@pytest.mark.parametrize("ncols", [32, 1536, 4096, 8192])
+def test_rms_norm_against_torch_f64(ncols):
+    x = synth.x_rows(ncols, 3)
+    w = synth.gain(ncols)
+    z64, z32, s64 = oracle.rms_norm(x, w)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x).double(), (ncols,),
+                                       weight=torch.from_numpy(w).double(), eps=EPS32).numpy()
+    assert np.all(np.abs(z64 - ref) <= 1e-14 * np.abs(ref) + 1e-300)
+    assert np.array_equal(z32, z64.astype(np.float32))
+
+
+@pytest.mark.parametrize("c", [2.0 ** -10, 0.75, -3.5])
+def test_rms_norm_constant_row_closed_form(c):
+    # x = c everywhere, w = 1: mean(x^2) = c^2 and z = c / sqrt(c^2 + eps).  The 2^-10 case
+    # makes eps (1e-6f) comparable to c^2 = 9.5e-7, so where eps enters is visible.
+    n = 256
+    x = np.full((1, n), c, dtype=np.float32)
+    w = np.ones(n, dtype=np.float32)
+    z64, _, _ = oracle.rms_norm(x, w)
+    getcontext().prec = 50
+    dc = Decimal(c)
+    want = float(dc / (dc * dc + Decimal(EPS32)).sqrt())
+    assert np.all(np.abs(z64 - want) <= 4e-16 * abs(want))
+
+
+def test_rms_norm_invariants():
+    n = 4096
+    x = synth.x_rows(n, 2)
+    w = synth.gain(n)
+    z64, _, s64 = oracle.rms_norm(x, w)
+    # column permutation commutes (the exactly rounded sum does not depend on order)
+    perm = np.random.default_rng(5).permutation(n)
+    zp, _, sp = oracle.rms_norm(x[:, perm], w[perm])
+    assert np.array_equal(zp, z64[:, perm]) and np.array_equal(sp, s64)
+    # the gain enters linearly
+    z2, _, _ = oracle.rms_norm(x, (w.astype(np.float64) * 2).astype(np.float32))
+    assert np.array_equal(z2, 2 * z64)
+    # mean((z / w)^2) = ms / (ms + eps), ms = mean(x^2)
+    for r in range(2):
+        ms = math.fsum(x[r].astype(np.float64) ** 2) / n
+        got = np.mean((z64[r] / w.astype(np.float64)) ** 2)
+        assert abs(got - ms / (ms + EPS32)) <= 1e-12
+    # rows are independent
+    z1, _, _ = oracle.rms_norm(x[1:2], w)
+    assert np.array_equal(z1[0], z64[1])
+
+
+# -------------------------------------------------------------------------------- GEMVs
+
+def _e4m3_lib(W):
+    return torch.from_numpy(np.ascontiguousarray(W)).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+
+
+def _q8_0_lib(Wq, in_f):
+    out_f = Wq.shape[0]
+    nb = in_f // 32
+    blk = Wq[:, :nb * 34].reshape(out_f, nb, 34)
+    scale = blk[:, :, 0:2].copy().view(np.float16).astype(np.float64).reshape(out_f, nb)
+    q = blk[:, :, 2:].view(np.int8).astype(np.float64)
+    return (q * scale[:, :, None]).reshape(out_f, in_f)
+
+
+def _act(in_f, m, seed):
+    x = np.stack([synth.f32(seed + t, in_f) for t in range(m)])
+    return oracle.quantize_q8_1(x)
+
+
+def _dequant(kind, in_f, out_f, seed):
+    """Weights of one container and their values via library decoders (f64 [out_f, in_f])."""
+    if kind == "q8_0":
+        Wq = synth.q8_0_weights(out_f, in_f)
+        return Wq, _q8_0_lib(Wq, in_f), None
+    W = synth.e4m3(seed, out_f * in_f).reshape(out_f, in_f)
+    vals = _e4m3_lib(W)
+    if kind == "e4m3":
+        return W, vals * 2.0 ** -4, None
+    g = synth.blk128_grid(out_f, in_f)
+    gexp = np.repeat(np.repeat(g.astype(np.float64), 128, 0), 128, 1)[:out_f, :in_f]
+    return W, vals * gexp, g
+
+
+def _run(kind, W, grid, qs, d, in_f, out_f, rows=None):
+    if kind == "q8_0":
+        return oracle.gemv_q8_0(W, W.shape[1], qs, d, in_f, out_f, rows)
+    if kind == "e4m3":
+        return oracle.gemv_e4m3(W, in_f, 2.0 ** -4, qs, d, in_f, out_f, rows)
+    return oracle.gemv_e4m3_blk128(W, in_f, grid, qs, d, in_f, out_f, rows)
+
+
+KINDS = ["q8_0", "e4m3", "blk128"]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("out_f,in_f,m", [(1, 32, 1), (3, 96, 2), (130, 160, 1), (131, 288, 2)])
+def test_gemv_exact_rational_bruteforce(kind, out_f, in_f, m):
+    W, w_hat, grid = _dequant(kind, in_f, out_f, seed=100 + in_f)
+    qs, d = _act(in_f, m, seed=200 + out_f)
+    y, A = _run(kind, W, grid, qs, d, in_f, out_f)
+    a_hat = [[Fraction(float(d[t, k // 32])) * int(qs[t, k]) for k in range(in_f)]
+             for t in range(m)]
+    rows = range(out_f) if out_f <= 3 else [0, 1, 63, 127, 128, 129, out_f - 1]
+    for t in range(m):
+        for r in rows:
+            terms = [Fraction(float(w_hat[r, k])) * a_hat[t][k] for k in range(in_f)]
+            exact = sum(terms)
+            aabs = sum(abs(v) for v in terms)
+            tol = Fraction(in_f) * Fraction(1, 2 ** 52) * aabs
+            assert abs(Fraction(float(y[t, r])) - exact) <= tol, (kind, t, r)
+            assert abs(Fraction(float(A[t, r])) - aabs) <= tol, (kind, t, r)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_against_numpy_matmul(kind):
+    out_f, in_f, m = 257, 640, 2
+    W, w_hat, grid = _dequant(kind, in_f, out_f, seed=7)
+    qs, d = _act(in_f, m, seed=8)
+    a_hat = qs.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    ref = a_hat @ w_hat.T
+    y, A = _run(kind, W, grid, qs, d, in_f, out_f)
+    assert np.all(np.abs(y - ref) <= 1e-12 * A)
+    assert np.all(A >= np.abs(y))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_one_hot_activation_reads_one_column(kind):
+    out_f, in_f = 300, 384
+    W, w_hat, grid = _dequant(kind, in_f, out_f, seed=9)
+    for k0 in (0, 31, 32, 127, 128, 200, in_f - 1):
+        qs = np.zeros((1, in_f), dtype=np.int8)
+        qs[0, k0] = 1
+        d = np.ones((1, in_f // 32), dtype=np.float32)
+        y, A = _run(kind, W, grid, qs, d, in_f, out_f)
+        assert np.array_equal(y[0], w_hat[:, k0]), (kind, k0)
+        assert np.array_equal(A[0], np.abs(w_hat[:, k0]))
+
+
+def test_gemv_q8_0_page_scale_bytes():
+    # gemv_e4m3_bench.rs, synth_q8_0: bytes 0x00, 0x14 at the block head are f16 2^-10.
+    in_f = 64
+    W = np.zeros((1, 68), dtype=np.uint8)
+    for b in range(2):
+        W[0, 34 * b] = 0x00
+        W[0, 34 * b + 1] = 0x14
+        W[0, 34 * b + 2: 34 * b + 34] = np.arange(1, 33, dtype=np.uint8) * (1 + b)
+    qs = np.ones((1, in_f), dtype=np.int8)
+    d = np.ones((1, 2), dtype=np.float32)
+    y, _ = oracle.gemv_q8_0(W, 68, qs, d, in_f, 1)
+    assert y[0, 0] == 2.0 ** -10 * (528 + 2 * 528)
+
+
+def test_gemv_constant_grid_equals_per_tensor():
+    out_f, in_f = 300, 640
+    W = synth.e4m3(21, out_f * in_f).reshape(out_f, in_f)
+    qs, d = _act(in_f, 2, seed=22)
+    grid = np.full(((out_f + 127) // 128, (in_f + 127) // 128), 2.0 ** -3, dtype=np.float32)
+    yb, Ab = oracle.gemv_e4m3_blk128(W, in_f, grid, qs, d, in_f, out_f)
+    ye, Ae = oracle.gemv_e4m3(W, in_f, 2.0 ** -3, qs, d, in_f, out_f)
+    assert np.array_equal(yb, ye) and np.array_equal(Ab, Ae)
+
+
+def test_gemv_all_ones_weights_sum_the_activation():
+    out_f, in_f = 5, 512
+    W = np.full((out_f, in_f), 0x38, dtype=np.uint8)  # e4m3 1.0
+    qs, d = _act(in_f, 1, seed=23)
+    y, _ = oracle.gemv_e4m3(W, in_f, 1.0, qs, d, in_f, out_f)
+    want = math.fsum(float(d[0, k // 32]) * int(qs[0, k]) for k in range(in_f))
+    assert np.all(np.abs(y[0] - want) <= 1e-13 * abs(want))
+
+
+def test_gemv_row_stride_and_row_range():
+    out_f, in_f, pad = 40, 256, 48
+    W = synth.e4m3(31, out_f * in_f).reshape(out_f, in_f)
+    Wp = np.zeros((out_f, in_f + pad), dtype=np.uint8)
+    Wp[:, :in_f] = W
+    Wp[:, in_f:] = 0x7F  # padding is never read (it would be refused as NaN)
+    qs, d = _act(in_f, 1, seed=32)
+    y, A = oracle.gemv_e4m3(W, in_f, 0.5, qs, d, in_f, out_f)
+    yp, Ap = oracle.gemv_e4m3(Wp, in_f + pad, 0.5, qs, d, in_f, out_f)
+    assert np.array_equal(y, yp)
+    ys, _ = oracle.gemv_e4m3(W, in_f, 0.5, qs, d, in_f, out_f, rows=(10, 17))
+    assert np.array_equal(ys[0, 10:17], y[0, 10:17]) and np.all(np.isnan(ys[0, :10]))
+
+
+def test_gemv_refuses_nan_codes():
+    out_f, in_f = 2, 64
+    W = np.full((out_f, in_f), 0x38, dtype=np.uint8)
+    W[1, 5] = 0xFF
+    qs, d = _act(in_f, 1, seed=1)
+    with pytest.raises(ValueError):
+        oracle.gemv_e4m3(W, in_f, 1.0, qs, d, in_f, out_f)
+    Wq = np.zeros((1, 34), dtype=np.uint8)
+    Wq[0, 1] = 0x7C  # f16 +inf
+    with pytest.raises(ValueError):
+        oracle.gemv_q8_0(Wq, 34, qs[:, :32], d[:, :1], 32, 1)
