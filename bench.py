@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Bench: the m=1 decode matvec hot path on one MI355X, DRAM-cold.
+
+One step = for each 27B-class projection shape [out_f, in_f] in {5120x5120, 17408x5120,
+5120x17408} and for each weight container (per-tensor e4m3, block-128 e4m3, Q8_0), in that
+interleaved order: the fused producer rmsnorm_q8_1 on the f32 activation row, then the GEMV on
+the next rotated copy of that container's weights -- 9 producer + 9 GEMV launches.
+(gemv_e4m3_bench.rs: the three arms interleaved per iteration, each on its own weight copies,
+each block-128 grid rotating with its copy; q8_fuse_gate.rs: the fused producer.)
+
+DRAM-cold: every (shape, container) owns max(2, ceil(2 * 256 MiB / copy_bytes)) byte-identical
+weight copies and launches rotate through them, so no launch finds its weights in the 256 MB
+last-level cache (the page's own copies formula would fit two 89 MB copies inside it).
+
+value = weight-plane bytes of the step / step time (GB/s); the JSON line also carries per
+(shape, container) microseconds per GEMV from HIP events, the roofline of the dominant GEMV
+kernel and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/GEMV and weight-stream HBM GB/s (% of peak) at m=1, 27B-class shapes, DRAM-cold"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+LLC_BYTES = 256 * 1024 * 1024  # MI355X last-level (Infinity) cache
+SHAPES = [(5120, 5120), (17408, 5120), (5120, 17408)]  # [out_f, in_f]
+ARMS = ["e4m3", "blk128", "q8_0"]
+SCALE = 2.0 ** -4
+EPS = 1e-6
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_bytes(arm: str, out_f: int, in_f: int) -> int:
+    return out_f * (in_f // 32) * 34 if arm == "q8_0" else out_f * in_f
+
+
+def grid_bytes(arm: str, out_f: int, in_f: int) -> int:
+    return 4 * ((out_f + 127) // 128) * ((in_f + 127) // 128) if arm == "blk128" else 0
+
+
+def algorithmic_bytes(arm: str, out_f: int, in_f: int, m: int = 1) -> int:
+    """Bytes one GEMV launch must move: weights (+ grid) + q8_1 activation + f32 output."""
+    return (weight_bytes(arm, out_f, in_f) + grid_bytes(arm, out_f, in_f)
+            + m * (in_f + 4 * (in_f // 32)) + 4 * m * out_f)
+
+
+def n_copies(nbytes: int) -> int:
+    return max(2, math.ceil(2 * LLC_BYTES / nbytes))
+
+
+class Arm:
+    """Rotated device copies of one container at one shape, plus its launch."""
+
+    def __init__(self, fg, torch, arm, out_f, in_f, dev):
+        import synth
+        self.fg, self.arm, self.out_f, self.in_f = fg, arm, out_f, in_f
+        if arm == "q8_0":
+            host = synth.q8_0_weights(out_f, in_f)
+        else:
+            host = synth.e4m3_weights(out_f, in_f)
+        self.row_bytes = host.shape[1]
+        first = torch.from_numpy(host).to(dev)
+        self.copies = n_copies(weight_bytes(arm, out_f, in_f))
+        self.W = [first] + [first.clone() for _ in range(self.copies - 1)]
+        self.grids = None
+        if arm == "blk128":
+            g = torch.from_numpy(synth.blk128_grid(out_f, in_f)).to(dev)
+            self.grids = [g] + [g.clone() for _ in range(self.copies - 1)]
+            self.grid_cols = g.shape[1]
+        self.y = torch.empty(out_f, device=dev)
+        self.i = 0
+
+    def launch(self, qs, d):
+        c = self.i % self.copies
+        self.i += 1
+        fg = self.fg
+        if self.arm == "q8_0":
+            fg.gemv_q8_0_q81(self.W[c], self.row_bytes, qs, d, self.y, 1, self.in_f, self.out_f)
+        elif self.arm == "e4m3":
+            fg.gemv_e4m3_q81(self.W[c], self.row_bytes, SCALE, qs, d, self.y, 1, self.in_f,
+                             self.out_f)
+        else:
+            fg.gemv_e4m3_blk128_q81(self.W[c], self.row_bytes, self.grids[c], self.grid_cols, qs,
+                                    d, self.y, 1, self.in_f, self.out_f)
+
+
+def cpu_baseline(shapes, arms, threads: int):
+    """The oracle, as it stands, over one full step on `threads` host threads (row ranges)."""
+    import oracle
+    import synth
+    work = []
+    for out_f, in_f in shapes:
+        x, w = synth.x_rows(in_f, 1), synth.gain(in_f)
+        for arm in arms:
+            W = synth.q8_0_weights(out_f, in_f) if arm == "q8_0" else synth.e4m3_weights(out_f, in_f)
+            g = synth.blk128_grid(out_f, in_f) if arm == "blk128" else None
+            work.append((arm, out_f, in_f, x, w, W, g))
+    pool = cf.ThreadPoolExecutor(max_workers=threads)
+
+    def gemv(arm, out_f, in_f, W, g, qs, d, rows):
+        if arm == "q8_0":
+            return oracle.gemv_q8_0(W, W.shape[1], qs, d, in_f, out_f, rows)
+        if arm == "e4m3":
+            return oracle.gemv_e4m3(W, in_f, SCALE, qs, d, in_f, out_f, rows)
+        return oracle.gemv_e4m3_blk128(W, in_f, g, qs, d, in_f, out_f, rows)
+
+    t0 = time.perf_counter()
+    wbytes = 0
+    for arm, out_f, in_f, x, w, W, g in work:
+        ref = oracle.rmsnorm_q8_1(x, w)
+        qs, d = ref["qs"], ref["d"]
+        step = (out_f + threads - 1) // threads
+        futs = [pool.submit(gemv, arm, out_f, in_f, W, g, qs, d, (r, min(out_f, r + step)))
+                for r in range(0, out_f, step)]
+        for f in futs:
+            f.result()
+        wbytes += weight_bytes(arm, out_f, in_f)
+    secs = time.perf_counter() - t0
+    pool.shutdown()
+    return {"value": round(wbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "ms_per_step": round(secs * 1e3, 1),
+            "sample": "one full step: rmsnorm_q8_1 + the 9 GEMVs (3 shapes x 3 containers), "
+                      "f64 oracle, output rows split over host threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--kernel-iters", type=int, default=60,
+                    help="back-to-back launches per (shape, container) for per-kernel timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--shapes", default="all", help="comma list like 17408x5120 (out x in)")
+    ap.add_argument("--arms", default=",".join(ARMS))
+    ap.add_argument("--jsonl", default="", help="append per-(shape, container) rows here")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build measures one GPU's share; the matvec shards by output rows)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import fp8_gemv_amd as fg
+
+    shapes = SHAPES if args.shapes == "all" else [
+        tuple(int(v) for v in s.split("x")) for s in args.shapes.split(",")]
+    arms = [a for a in args.arms.split(",") if a]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    log(f"device {torch.cuda.get_device_name(dev)}; building rotated copies")
+
+    import synth
+    prod = {}
+    for out_f, in_f in shapes:
+        x = torch.from_numpy(synth.x_rows(in_f, 1)).to(dev)
+        w = torch.from_numpy(synth.gain(in_f)).to(dev)
+        qs = torch.empty(in_f, dtype=torch.int8, device=dev)
+        d = torch.empty(in_f // 32, device=dev)
+        prod[(out_f, in_f)] = (x, w, qs, d)
+    arm_objs = {}
+    for out_f, in_f in shapes:
+        for a in arms:
+            arm_objs[(out_f, in_f, a)] = Arm(fg, torch, a, out_f, in_f, dev)
+    torch.cuda.synchronize()
+    log("copies ready: " + ", ".join(f"{k[0]}x{k[1]} {k[2]}: {v.copies}" for k, v in arm_objs.items()))
+
+    def producer(key):
+        x, w, qs, d = prod[key]
+        fg.rmsnorm_q8_1(x, w, None, qs, d, key[1], 1, EPS)
+        return qs, d
+
+    def step():
+        for out_f, in_f in shapes:
+            for a in arms:
+                qs, d = producer((out_f, in_f))
+                arm_objs[(out_f, in_f, a)].launch(qs, d)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    step_wbytes = sum(weight_bytes(a, o, i) for (o, i, a) in arm_objs)
+    value = step_wbytes / (ms_per_step * 1e-3) / 1e9
+    log(f"step {ms_per_step:.3f} ms (host wall {wall_ms:.3f} ms), {value:.1f} GB/s of weights")
+
+    # Per-kernel timing: back-to-back launches of one GEMV over its rotated copies, bracketed
+    # by HIP events on the launch stream; the q8_1 activation is produced once before.
+    detail = {}
+    for (out_f, in_f, a), obj in arm_objs.items():
+        qs, d = producer((out_f, in_f))
+        for _ in range(min(obj.copies, 4)):
+            obj.launch(qs, d)
+        n = max(args.kernel_iters, obj.copies)
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record(stream)
+        for _ in range(n):
+            obj.launch(qs, d)
+        k1.record(stream)
+        torch.cuda.synchronize()
+        us = k0.elapsed_time(k1) * 1e3 / n
+        wb = weight_bytes(a, out_f, in_f)
+        detail[f"{a}@{out_f}x{in_f}"] = {
+            "us": round(us, 3), "weight_GBs": round(wb / us / 1e3, 1),
+            "pct_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1),
+            "alg_bytes": algorithmic_bytes(a, out_f, in_f), "copies": obj.copies, "launches": n}
+        log(f"{a:7s} {out_f}x{in_f}: {us:8.2f} us  {wb / us / 1e3:7.1f} GB/s")
+        if args.jsonl:
+            with open(args.jsonl, "a") as f:
+                f.write(json.dumps({"arm": a, "out_f": out_f, "in_f": in_f, **detail[f"{a}@{out_f}x{in_f}"]}) + "\n")
+
+    # Producer alone (latency-bound; the gate page's site widths).
+    prod_us = {}
+    for ncols in (1536, 4096, 8192):
+        x = torch.from_numpy(synth.x_rows(ncols, 1)).to(dev)
+        w = torch.from_numpy(synth.gain(ncols)).to(dev)
+        z = torch.empty(ncols, device=dev)
+        qs = torch.empty(ncols, dtype=torch.int8, device=dev)
+        d = torch.empty(ncols // 32, device=dev)
+        for variant in ("fused", "chain"):
+            def run():
+                if variant == "fused":
+                    fg.rmsnorm_q8_1(x, w, z, qs, d, ncols, 1, EPS)
+                else:
+                    fg.rms_norm_f32(x, w, z, ncols, 1, EPS)
+                    fg.quantize_q8_1(z, qs, d, 1, ncols)
+            for _ in range(3):
+                run()
+            k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0.record(stream)
+            for _ in range(50):
+                run()
+            k1.record(stream)
+            torch.cuda.synchronize()
+            prod_us[f"{variant}@{ncols}"] = round(k0.elapsed_time(k1) * 1e3 / 50, 3)
+
+    # Roofline of the dominant GEMV kernel (largest time per step).
+    dom_key = max(detail, key=lambda k: detail[k]["us"])
+    dom = detail[dom_key]
+    achieved = dom["alg_bytes"] / (dom["us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dom_key}
+
+    cpu = None
+    if not args.no_cpu:
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        log(f"cpu baseline: oracle over one step on {threads} threads")
+        cpu = cpu_baseline(shapes, arms, threads)
+        log(f"cpu baseline {cpu['ms_per_step']} ms/step = {cpu['value']} GB/s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3/int8 x int8 -> f32", "data": "synthetic",
+        "config": {"workload": "m=1 decode matvec step: rmsnorm_q8_1 + GEMV for e4m3, "
+                               "e4m3-blk128 and Q8_0 weights at [out_f,in_f] 5120x5120, "
+                               "17408x5120, 5120x17408, interleaved, DRAM-cold rotation",
+                   "m": 1, "shapes": [f"{o}x{i}" for o, i in shapes], "arms": arms,
+                   "eps": EPS, "e4m3_scale": SCALE},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "host_wall_ms_per_step": round(wall_ms, 4),
+        "gemv": detail, "producer_us": prod_us,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

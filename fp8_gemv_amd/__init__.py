@@ -1,0 +1,214 @@
+"""Python binding of the gfx950 m=1 decode matvec library (``libfp8_gemv.so``).
+
+Each function has the name and argument order of the C entry point in
+``include/fp8_gemv.h``.  The binding only marshals arguments: it checks that every tensor
+is a contiguous tensor of the right dtype on the current GPU and large enough for the sizes
+passed (the C side cannot see buffer sizes), turns tensors into device pointers, takes the
+current torch stream when none is given, and raises on a non-zero return code.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback of any kind, and
+importing this package fails if the library has not been built.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the process's HIP runtime before the library binds to it
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8_gemv.so")
+
+FP8GEMV_OK = 0
+FP8GEMV_ERR_NULL = -1
+FP8GEMV_ERR_SHAPE = -2
+FP8GEMV_ERR_ROW_BYTES = -3
+FP8GEMV_ERR_GRID = -4
+FP8GEMV_ERR_ALIGN = -5
+FP8GEMV_ERR_TOO_LARGE = -6
+FP8GEMV_MAX_IN_F = 65536
+FP8GEMV_MAX_M = 65535
+
+EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "gemv_q8_0_q81", "gemv_e4m3_q81",
+           "gemv_e4m3_blk128_q81", "fp8gemv_strerror")
+
+
+class Fp8GemvError(RuntimeError):
+    """A non-zero return code from the library."""
+
+    def __init__(self, fn: str, rc: int, msg: str):
+        super().__init__(f"{fn}: {msg} (rc={rc})")
+        self.rc = rc
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()' or python fp8_gemv_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    sig = {
+        "rms_norm_f32": [vp, vp, vp, i32, i32, f32, vp],
+        "quantize_q8_1": [vp, vp, vp, i32, i32, vp],
+        "rmsnorm_q8_1": [vp, vp, vp, vp, vp, i32, i32, f32, vp],
+        "gemv_q8_0_q81": [vp, i64, vp, vp, vp, i32, i32, i32, vp],
+        "gemv_e4m3_q81": [vp, i64, f32, vp, vp, vp, i32, i32, i32, vp],
+        "gemv_e4m3_blk128_q81": [vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = i32
+    lib.fp8gemv_strerror.argtypes = [i32]
+    lib.fp8gemv_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (for callers that marshal pointers themselves)."""
+    return _lib
+
+
+def strerror(rc: int) -> str:
+    return _lib.fp8gemv_strerror(int(rc)).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise Fp8GemvError(fn, rc, strerror(rc))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t, name: str, dtype, min_numel: int, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name}: has {t.numel()} elements, the sizes passed need {min_numel}")
+    return t.data_ptr()
+
+
+def _dev(t):
+    return t.device if isinstance(t, torch.Tensor) else None
+
+
+# ----------------------------------------------------------------------------- producer
+
+def rms_norm_f32(x, w, z, ncols: int, nrows: int, eps: float = 1e-6, stream=None) -> None:
+    """z[r, :] = x[r, :] * w / sqrt(mean(x[r, :]^2) + eps)  (first half of the chain)."""
+    dev = _dev(x)
+    rc = _lib.rms_norm_f32(_ptr(x, "x", torch.float32, ncols * nrows, dev),
+                           _ptr(w, "w", torch.float32, ncols, dev),
+                           _ptr(z, "z", torch.float32, ncols * nrows, dev),
+                           ncols, nrows, eps, _stream(stream))
+    _check("rms_norm_f32", rc)
+
+
+def quantize_q8_1(z, qs, d, nrows: int, ncols: int, stream=None) -> None:
+    """q8_1 of f32 rows: qs int8 [nrows, ncols], d f32 [nrows, ncols/32]."""
+    dev = _dev(z)
+    rc = _lib.quantize_q8_1(_ptr(z, "z", torch.float32, ncols * nrows, dev),
+                            _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
+                            _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
+                            nrows, ncols, _stream(stream))
+    _check("quantize_q8_1", rc)
+
+
+def rmsnorm_q8_1(x, w, z, qs, d, ncols: int, nrows: int, eps: float = 1e-6,
+                 stream=None) -> None:
+    """Fused producer: RMSNorm then q8_1 in one launch (z may be None)."""
+    dev = _dev(x)
+    rc = _lib.rmsnorm_q8_1(_ptr(x, "x", torch.float32, ncols * nrows, dev),
+                           _ptr(w, "w", torch.float32, ncols, dev),
+                           _ptr(z, "z", torch.float32, ncols * nrows, dev),
+                           _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
+                           _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
+                           ncols, nrows, eps, _stream(stream))
+    _check("rmsnorm_q8_1", rc)
+
+
+# -------------------------------------------------------------------------------- GEMVs
+
+def _w_numel(row_bytes: int, out_f: int, in_f: int, container_row: int) -> int:
+    # the last row only needs its used bytes
+    return (out_f - 1) * row_bytes + container_row if out_f >= 1 else 0
+
+
+def gemv_q8_0_q81(W, row_bytes: int, qs, d, y, m: int, in_f: int, out_f: int,
+                  stream=None) -> None:
+    """y[m, out_f] = Q8_0 weight rows W times the q8_1 activation (qs, d)."""
+    dev = _dev(W)
+    rc = _lib.gemv_q8_0_q81(_ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f,
+                                                                in_f // 32 * 34), dev),
+                            row_bytes,
+                            _ptr(qs, "qs", torch.int8, m * in_f, dev),
+                            _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
+                            _ptr(y, "y", torch.float32, m * out_f, dev),
+                            m, in_f, out_f, _stream(stream))
+    _check("gemv_q8_0_q81", rc)
+
+
+def gemv_e4m3_q81(W, row_bytes: int, scale: float, qs, d, y, m: int, in_f: int, out_f: int,
+                  stream=None) -> None:
+    """y[m, out_f] = scale * e4m3 weights W times the q8_1 activation (qs, d)."""
+    dev = _dev(W)
+    rc = _lib.gemv_e4m3_q81(_ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f),
+                                 dev),
+                            row_bytes, scale,
+                            _ptr(qs, "qs", torch.int8, m * in_f, dev),
+                            _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
+                            _ptr(y, "y", torch.float32, m * out_f, dev),
+                            m, in_f, out_f, _stream(stream))
+    _check("gemv_e4m3_q81", rc)
+
+
+def gemv_e4m3_blk128_q81(W, row_bytes: int, grid, grid_cols: int, qs, d, y, m: int, in_f: int,
+                         out_f: int, stream=None) -> None:
+    """y[m, out_f] = block-128-scaled e4m3 weights W times the q8_1 activation (qs, d)."""
+    dev = _dev(W)
+    rc = _lib.gemv_e4m3_blk128_q81(
+        _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f), dev), row_bytes,
+        _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
+        _ptr(qs, "qs", torch.int8, m * in_f, dev),
+        _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
+        _ptr(y, "y", torch.float32, m * out_f, dev),
+        m, in_f, out_f, _stream(stream))
+    _check("gemv_e4m3_blk128_q81", rc)
+
+
+# ------------------------------------------------------------------------- byte counts
+
+def e4m3_weight_bytes(out_f: int, in_f: int) -> int:
+    """Weight-plane bytes of a raw e4m3 matrix: one byte per weight."""
+    return out_f * in_f
+
+
+def q8_0_weight_bytes(out_f: int, in_f: int) -> int:
+    """Weight-plane bytes of a Q8_0 matrix: 34 bytes per 32 weights."""
+    return out_f * (in_f // 32) * 34
+
+
+def blk128_grid_bytes(out_f: int, in_f: int) -> int:
+    """Bytes of the f32 [ceil(out_f/128), ceil(in_f/128)] scale grid."""
+    return 4 * ((out_f + 127) // 128) * ((in_f + 127) // 128)

@@ -1,0 +1,104 @@
+// C ABI of the gfx950 matvec library: argument checks on the host, then one launch on the
+// caller's stream.  Nothing here allocates, synchronises or touches device memory.
+#include "../../include/fp8_gemv.h"
+#include "common.hpp"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int launch_rc(hipError_t e) { return e == hipSuccess ? FP8GEMV_OK : (int)e; }
+
+inline bool bad_cols(int ncols) { return ncols < 32 || ncols % 32 != 0; }
+
+int check_gemv_common(const void *W, const int8_t *qs, const float *d, float *y, int m,
+                      int in_f, int out_f) {
+  if (!W || !qs || !d || !y) return FP8GEMV_ERR_NULL;
+  if (m < 1 || out_f < 1 || bad_cols(in_f)) return FP8GEMV_ERR_SHAPE;
+  if (in_f > FP8GEMV_MAX_IN_F || m > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(qs, 16) || !aligned(d, 4) || !aligned(y, 4)) return FP8GEMV_ERR_ALIGN;
+  return FP8GEMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rms_norm_f32(const float *x, const float *w, float *z, int ncols, int nrows, float eps,
+                 void *stream) {
+  if (!x || !w || !z) return FP8GEMV_ERR_NULL;
+  if (nrows < 1 || bad_cols(ncols)) return FP8GEMV_ERR_SHAPE;
+  if (ncols > FP8GEMV_MAX_IN_F) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(z, 16)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_rms_norm(x, w, z, ncols, nrows, eps, (hipStream_t)stream));
+}
+
+int quantize_q8_1(const float *z, int8_t *qs, float *d, int nrows, int ncols, void *stream) {
+  if (!z || !qs || !d) return FP8GEMV_ERR_NULL;
+  if (nrows < 1 || bad_cols(ncols)) return FP8GEMV_ERR_SHAPE;
+  if (ncols > FP8GEMV_MAX_IN_F || nrows > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(z, 16) || !aligned(qs, 16) || !aligned(d, 4)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_quantize_q8_1(z, qs, d, nrows, ncols, (hipStream_t)stream));
+}
+
+int rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d, int ncols,
+                 int nrows, float eps, void *stream) {
+  if (!x || !w || !qs || !d) return FP8GEMV_ERR_NULL;
+  if (nrows < 1 || bad_cols(ncols)) return FP8GEMV_ERR_SHAPE;
+  if (ncols > FP8GEMV_MAX_IN_F) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(x, 16) || !aligned(w, 16) || (z && !aligned(z, 16)) || !aligned(qs, 16) ||
+      !aligned(d, 4))
+    return FP8GEMV_ERR_ALIGN;
+  return launch_rc(
+      fp8gemv::launch_rmsnorm_q8_1(x, w, z, qs, d, ncols, nrows, eps, (hipStream_t)stream));
+}
+
+int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
+                  int m, int in_f, int out_f, void *stream) {
+  const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);
+  if (rc) return rc;
+  if (row_bytes < (int64_t)(in_f / 32) * 34) return FP8GEMV_ERR_ROW_BYTES;
+  if (!aligned(W, 2) || row_bytes % 2 != 0) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_gemv_q8_0(static_cast<const uint8_t *>(W), row_bytes, qs, d,
+                                             y, m, in_f, out_f, (hipStream_t)stream));
+}
+
+int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
+                  const float *d, float *y, int m, int in_f, int out_f, void *stream) {
+  const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);
+  if (rc) return rc;
+  if (row_bytes < in_f) return FP8GEMV_ERR_ROW_BYTES;
+  if (!aligned(W, 16) || row_bytes % 16 != 0) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_gemv_e4m3(W, row_bytes, scale, nullptr, 0, false, qs, d, y, m,
+                                             in_f, out_f, (hipStream_t)stream));
+}
+
+int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid, int grid_cols,
+                         const int8_t *qs, const float *d, float *y, int m, int in_f, int out_f,
+                         void *stream) {
+  const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);
+  if (rc) return rc;
+  if (!grid) return FP8GEMV_ERR_NULL;
+  if (grid_cols != (in_f + 127) / 128) return FP8GEMV_ERR_GRID;
+  if (row_bytes < in_f) return FP8GEMV_ERR_ROW_BYTES;
+  if (!aligned(W, 16) || row_bytes % 16 != 0 || !aligned(grid, 4)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_gemv_e4m3(W, row_bytes, 1.0f, grid, grid_cols, true, qs, d, y,
+                                             m, in_f, out_f, (hipStream_t)stream));
+}
+
+const char *fp8gemv_strerror(int rc) {
+  switch (rc) {
+    case FP8GEMV_OK: return "ok";
+    case FP8GEMV_ERR_NULL: return "a required pointer is NULL";
+    case FP8GEMV_ERR_SHAPE: return "bad shape: columns must be a positive multiple of 32, rows >= 1";
+    case FP8GEMV_ERR_ROW_BYTES: return "row_bytes is below the container minimum";
+    case FP8GEMV_ERR_GRID: return "grid_cols must equal ceil(in_f / 128)";
+    case FP8GEMV_ERR_ALIGN: return "a pointer or row stride breaks the required alignment";
+    case FP8GEMV_ERR_TOO_LARGE: return "a size exceeds the library limit";
+    default: break;
+  }
+  if (rc > 0) return hipGetErrorString((hipError_t)rc);
+  return "unknown error";
+}
+
+}  // extern "C"

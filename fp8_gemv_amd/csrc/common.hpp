@@ -1,0 +1,72 @@
+// Shared device helpers and the internal launcher interface of the gfx950 matvec library.
+// Everything here is written for CDNA4 wave64; there is no other target.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8gemv {
+
+constexpr int kWave = 64;
+constexpr int kMaxInF = 65536;  // FP8GEMV_MAX_IN_F of the public header
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ cross-lane sums ----
+// DPP controls (GFX9 encoding).
+constexpr int kQuadPerm1032 = 0xB1;  // lanes {1,0,3,2} within each quad
+constexpr int kQuadPerm2301 = 0x4E;  // lanes {2,3,0,1} within each quad
+constexpr int kRowRor4 = 0x124;      // rotate right by 4 within each row of 16
+constexpr int kRowRor8 = 0x128;      // rotate right by 8 within each row of 16
+
+// Full row and bank masks, bound_ctrl off: every lane has a valid source for these patterns.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over all 64 lanes.  Within each row of 16 lanes a DPP butterfly (xor 1, xor 2, then
+// rotations by 4 and 8) leaves the row sum in every lane; the four row sums are then read
+// from lanes 0, 16, 32, 48 and added in that fixed order.  The result is wave-uniform and
+// depends only on the lane values, never on timing.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<kQuadPerm1032>(v);
+  v += dpp_f32<kQuadPerm2301>(v);
+  v += dpp_f32<kRowRor4>(v);
+  v += dpp_f32<kRowRor8>(v);
+  const int iv = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// ----------------------------------------------------------------------- loads ----
+// 16-byte streaming load of weight bytes: read once, never reused, so marked non-temporal.
+__device__ __forceinline__ int4_t load_stream16(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const int4_t *>(p));
+}
+
+}  // namespace fp8gemv
+
+// --------------------------------------------------------------- internal launchers ----
+// Host-side launchers, one per kernel family; arguments are validated by the C ABI layer
+// before these run.  Each returns the hipError_t of the launch.
+namespace fp8gemv {
+
+hipError_t launch_rms_norm(const float *x, const float *w, float *z, int ncols, int nrows,
+                           float eps, hipStream_t s);
+hipError_t launch_quantize_q8_1(const float *z, int8_t *qs, float *d, int nrows, int ncols,
+                                hipStream_t s);
+hipError_t launch_rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d,
+                               int ncols, int nrows, float eps, hipStream_t s);
+hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
+                            int grid_cols, bool blk128, const int8_t *qs, const float *d,
+                            float *y, int m, int in_f, int out_f, hipStream_t s);
+hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
+                            const float *d, float *y, int m, int in_f, int out_f, hipStream_t s);
+
+}  // namespace fp8gemv

@@ -1,0 +1,250 @@
+// m=1 decode GEMV over ggml Q8_0 weight rows against a q8_1 activation.
+//
+// Source: docs.rs, memra-engine 0.125.0, src/bin/gemv_e4m3_bench.rs -- module doc sections
+// QUESTION and THE COMPARISON (arm Q8_0: 34 bytes per 32 weights, an fp16 scale then 32
+// int8, row_bytes = in_f/32*34, the 1.0625 byte/weight floor) and `synth_q8_0` (the scale
+// is little-endian at bytes 0..1 of each block).
+//
+// y[t, r] = sum_b fp16(scale[r, b]) * d_a[t, b] * sum_{i<32} qw[r, b, i] * qs[t, 32b + i]
+//
+// gfx950 design (the page's kernel is a CUDA warp-per-row MMVQ with dp4a; this one is not a
+// translation of it).  The difficulty is that 34-byte blocks do not line up with 16-byte
+// loads.  Fast path (in_f % 256 == 0, so every row is 17*in_f/256 whole 16-byte chunks and
+// every row starts the block pattern at a chunk boundary):
+//   * Lane l of a wave streams chunk 64*win + l of the row with one 16-byte non-temporal
+//     load: fully coalesced, every weight byte fetched exactly once.
+//   * The activation is staged in LDS "in the shape of a Q8_0 row": 34 bytes per block, two
+//     zero bytes where the weight row has its fp16 scale, then the 32 qs.  A weight chunk and
+//     the activation chunk at the same offset line up byte for byte, so four v_dot4_i32_i8
+//     give the integer products of the chunk, and the scale bytes meet zeros.
+//   * No dword mixes quantised bytes of two blocks (block boundaries are 34 bytes apart and
+//     the 2-byte scale sits between them), so a chunk's four dwords split into a prefix that
+//     belongs to block b0 and a suffix that belongs to b0 + 1; the two exact int32 sums are
+//     scaled separately.
+//   * A chunk contains at most one block scale.  The lane holding it converts it
+//     (fp16 -> f32, times the activation scale d_a[b]) and publishes it in a per-wave LDS
+//     table; the lanes that need it read it back after a wave-local fence.
+// Generic path (any in_f % 32 == 0): one lane per block, 2-byte loads; correct, not tuned.
+// Row t = blockIdx.y of the activation runs identical code, so each activation row of an
+// m-row call is bit-identical to an m=1 call on that row.
+#include "common.hpp"
+
+namespace fp8gemv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBlkBytes = 34;
+
+__host__ __device__ constexpr int chunks_per_row(int in_f) { return in_f / 32 * kBlkBytes / 16; }
+__host__ __device__ constexpr int windows_per_row(int in_f) {
+  return (chunks_per_row(in_f) + kWave - 1) / kWave;
+}
+
+// LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2],
+// then one scale table of nb + 2 floats per (wave, row).
+template <int RPW>
+__host__ __device__ constexpr size_t fast_lds_bytes(int in_f) {
+  return (size_t)windows_per_row(in_f) * 1024 + (size_t)(in_f / 32 + 2) * 4 * (1 + kWaves * RPW);
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int RPW, int U>
+__global__ __launch_bounds__(kThreads) void k_gemv_q8_0_fast(
+    const uint8_t *__restrict__ W, int64_t row_bytes, const int8_t *__restrict__ qs,
+    const float *__restrict__ d, float *__restrict__ y, int in_f, int out_f) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int nb = in_f / 32;
+  const int cpr = chunks_per_row(in_f);
+  const int nwin = windows_per_row(in_f);
+  uint8_t *shaped = lds;                                            // nwin * 1024 bytes
+  float *dsc = reinterpret_cast<float *>(lds + (size_t)nwin * 1024);  // nb + 2
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  float *stab = dsc + (nb + 2) * (1 + wave * RPW);  // RPW tables of nb + 2 floats
+  const int rbase = (blockIdx.x * kWaves + wave) * RPW;
+
+  const uint8_t *wrow[RPW];
+  bool rok[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    rok[r] = rbase + r < out_f;
+    wrow[r] = W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + lane * 16;
+  }
+
+  // First batch of weight loads, issued before the activation is staged.
+  int4_t wv[U][RPW];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      wv[u][r] = (int4_t){0, 0, 0, 0};
+      if (rok[r] && u * kWave + lane < cpr) wv[u][r] = load_stream16(wrow[r] + u * 1024);
+    }
+  }
+
+  // Stage the activation in the shape of a Q8_0 row (zeros at the scale bytes and in the
+  // padding past the row), and the block scales d_a.
+  {
+    const int8_t *qa = qs + (int64_t)t * in_f;
+    uint16_t *sh16 = reinterpret_cast<uint16_t *>(shaped);
+    for (int i = threadIdx.x; i < nwin * 512; i += kThreads) sh16[i] = 0;
+    __syncthreads();
+    for (int b = threadIdx.x; b < nb; b += kThreads) {
+      const int4_t q0 = *reinterpret_cast<const int4_t *>(qa + 32 * b);
+      const int4_t q1 = *reinterpret_cast<const int4_t *>(qa + 32 * b + 16);
+      uint16_t *dst = sh16 + (kBlkBytes * b + 2) / 2;  // 2-byte aligned
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dst[2 * j] = (uint16_t)(q0[j] & 0xFFFF);
+        dst[2 * j + 1] = (uint16_t)((uint32_t)q0[j] >> 16);
+        dst[8 + 2 * j] = (uint16_t)(q1[j] & 0xFFFF);
+        dst[8 + 2 * j + 1] = (uint16_t)((uint32_t)q1[j] >> 16);
+      }
+    }
+    const float *da = d + (int64_t)t * nb;
+    for (int b = threadIdx.x; b < nb + 2; b += kThreads) dsc[b] = (b < nb) ? da[b] : 0.0f;
+    __syncthreads();
+  }
+
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+
+  for (int w0 = 0; w0 < nwin; w0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int win = w0 + u;
+      if (win >= nwin) break;
+      const int c = win * kWave + lane;  // chunk index within the row
+      const bool live = c < cpr;
+      // Chunk geometry (the same for every row): bytes [p0, p0 + 16) of the row.
+      const int p0 = 16 * c;
+      const int b0 = p0 / kBlkBytes;              // block of the first byte
+      const int o = p0 - kBlkBytes * b0;          // offset inside that block, even, 0..32
+      const int hb = b0 + (o != 0);               // block whose scale may start in the chunk
+      const int hpos = kBlkBytes * hb - p0;       // its byte offset inside the chunk
+      const bool has_scale = live && hpos <= 14;
+      // dwords j < nlo hold quants of b0 (or its scale); the rest belong to b0 + 1.
+      const int nlo = o <= 20 ? 4 : (o <= 24 ? 3 : (o <= 28 ? 2 : 1));
+      const int4_t a = *reinterpret_cast<const int4_t *>(shaped + p0);  // zero past the row
+      const float da_h = dsc[live ? hb : 0];  // hb <= nb for a chunk inside the row
+
+      // Publish the scale that starts in this chunk: fp16 -> f32, times d_a.
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if (has_scale) {
+          const int4_t w = wv[u][r];
+          const int q = hpos >> 2;
+          const uint32_t dw = q == 0 ? w[0] : (q == 1 ? w[1] : (q == 2 ? w[2] : w[3]));
+          const uint16_t hbits = (hpos & 2) ? (uint16_t)(dw >> 16) : (uint16_t)(dw & 0xFFFF);
+          stab[r * (nb + 2) + hb] = (float)__builtin_bit_cast(_Float16, hbits) * da_h;
+        }
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int4_t w = wv[u][r];
+        const int t1 = __builtin_amdgcn_sdot4(w[0], a[0], 0, false);
+        const int t2 = __builtin_amdgcn_sdot4(w[1], a[1], t1, false);
+        const int t3 = __builtin_amdgcn_sdot4(w[2], a[2], t2, false);
+        const int t4 = __builtin_amdgcn_sdot4(w[3], a[3], t3, false);
+        const int s_lo = nlo == 4 ? t4 : (nlo == 3 ? t3 : (nlo == 2 ? t2 : t1));
+        const int s_hi = t4 - s_lo;
+        const float *tab = stab + r * (nb + 2);
+        const float S0 = live ? tab[b0] : 0.0f;
+        const float S1 = (live && nlo < 4) ? tab[b0 + 1] : 0.0f;
+        acc[r] = fmaf((float)s_lo, S0, acc[r]);
+        acc[r] = fmaf((float)s_hi, S1, acc[r]);
+      }
+    }
+    const int nxt = w0 + U;
+    if (nxt < nwin) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          wv[u][r] = (int4_t){0, 0, 0, 0};
+          if (rok[r] && (nxt + u) * kWave + lane < cpr)
+            wv[u][r] = load_stream16(wrow[r] + (int64_t)(nxt + u) * 1024);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float s = wave_sum(acc[r]);
+    if (lane == 0 && rok[r]) y[(int64_t)t * out_f + rbase + r] = s;
+  }
+}
+
+// Generic path: one wave per row, one lane per 34-byte block, 2-byte loads (W and row_bytes
+// need only be 2-byte aligned).
+__global__ __launch_bounds__(kThreads) void k_gemv_q8_0_generic(
+    const uint8_t *__restrict__ W, int64_t row_bytes, const int8_t *__restrict__ qs,
+    const float *__restrict__ d, float *__restrict__ y, int in_f, int out_f) {
+  const int nb = in_f / 32;
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (row >= out_f) return;  // whole wave exits together
+  const uint16_t *wr = reinterpret_cast<const uint16_t *>(W + (int64_t)row * row_bytes);
+  const int8_t *qa = qs + (int64_t)t * in_f;
+  const float *da = d + (int64_t)t * nb;
+  float acc = 0.0f;
+  for (int b = lane; b < nb; b += kWave) {
+    const uint16_t *blk = wr + b * (kBlkBytes / 2);
+    const uint16_t hbits = blk[0];
+    int isum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t wq = (uint32_t)blk[1 + 2 * j] | ((uint32_t)blk[2 + 2 * j] << 16);
+      const int aq = *reinterpret_cast<const int *>(qa + 32 * b + 4 * j);
+      isum = __builtin_amdgcn_sdot4((int)wq, aq, isum, false);
+    }
+    const float S = (float)__builtin_bit_cast(_Float16, hbits) * da[b];
+    acc = fmaf((float)isum, S, acc);
+  }
+  const float s = wave_sum(acc);
+  if (lane == 0) y[(int64_t)t * out_f + row] = s;
+}
+
+template <int RPW, int U>
+hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, const float *d,
+                       float *y, int m, int in_f, int out_f, hipStream_t s) {
+  auto kern = k_gemv_q8_0_fast<RPW, U>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)fast_lds_bytes<RPW>(kMaxInF));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int rows_per_wg = kWaves * RPW;
+  const dim3 g((out_f + rows_per_wg - 1) / rows_per_wg, m);
+  hipLaunchKernelGGL(kern, g, dim3(kThreads), fast_lds_bytes<RPW>(in_f), s, W, row_bytes, qs, d,
+                     y, in_f, out_f);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
+                            const float *d, float *y, int m, int in_f, int out_f, hipStream_t s) {
+  const bool fast = (in_f % 256 == 0) && (row_bytes % 16 == 0) &&
+                    ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
+  if (fast) return launch_fast<2, 4>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+  const dim3 g((out_f + kWaves - 1) / kWaves, m);
+  hipLaunchKernelGGL(k_gemv_q8_0_generic, g, dim3(kThreads), 0, s, W, row_bytes, qs, d, y, in_f,
+                     out_f);
+  return hipGetLastError();
+}
+
+}  // namespace fp8gemv

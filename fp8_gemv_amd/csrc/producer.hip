@@ -1,0 +1,194 @@
+// The activation producer: RMSNorm of an f32 row and its q8_1 quantisation.
+//
+// Source: docs.rs, memra-engine 0.125.0, src/bin/q8_fuse_gate.rs -- module doc and
+// `run_shape`: the two-launch chain rms_norm(x, w, z, ncols, nrows, eps) -> quantize_q8_1(z)
+// and the fused one-launch producer that still writes z and must give byte-identical z, qs
+// and d.  Byte identity holds here by construction: the chain kernels and the fused kernel
+// call the same device functions (row_scale for the RMS factor, z_value for z, quant_group
+// for a 32-block) with the same workgroup shape, and quantisation of a block depends only on
+// that block's 32 values.
+//
+// Numerics (this file is compiled with -ffp-contract=off):
+//   ss  = sum_j x_j^2, every square exact in f64, accumulated as a double-double and rounded
+//         once to f64, so ss is the correctly rounded sum except in vanishingly rare ties;
+//   s   = 1 / sqrt(ss / ncols + eps)                        (f64, IEEE div and sqrt)
+//   z_j = (float)(((double)x_j * (double)w_j) * s)          (x_j * w_j is exact in f64)
+//   q8_1 per 32-block in f32: d = amax / 127, id = d ? 1 / d : 0, q = roundf(z * id).
+#include "common.hpp"
+
+namespace fp8gemv {
+namespace {
+
+constexpr int kThreads = 256;            // 4 waves per row
+constexpr int kColsPerPass = kThreads * 4;  // each thread owns 4 consecutive columns
+
+// Exact sum and rounding error of a + b (Knuth's TwoSum; needs no contraction).
+__device__ __forceinline__ void two_sum(double a, double b, double &s, double &e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+__device__ __forceinline__ void dd_add(double &hi, double &lo, double ohi, double olo) {
+  double s, e;
+  two_sum(hi, ohi, s, e);
+  hi = s;
+  lo = (lo + olo) + e;
+}
+
+// 1 / sqrt(mean(x^2) + eps) for one row, computed by the whole workgroup; every thread
+// returns the same value.  `red` is LDS scratch for 2 doubles per wave.
+__device__ double row_scale(const float *__restrict__ x, int ncols, float eps, double *red) {
+  double hi = 0.0, lo = 0.0;
+  for (int j = threadIdx.x * 4; j < ncols; j += kColsPerPass) {
+    const float4 v = *reinterpret_cast<const float4 *>(x + j);
+    const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double p = (double)e4[i] * (double)e4[i];
+      double s, e;
+      two_sum(hi, p, s, e);
+      hi = s;
+      lo += e;
+    }
+  }
+  // Butterfly over the wave: both partners of a pair compute the same (commutative) result.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double ohi = __shfl_xor(hi, off);
+    const double olo = __shfl_xor(lo, off);
+    dd_add(hi, lo, ohi, olo);
+  }
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) {
+    red[2 * wave] = hi;
+    red[2 * wave + 1] = lo;
+  }
+  __syncthreads();
+  double thi = red[0], tlo = red[1];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) dd_add(thi, tlo, red[2 * w], red[2 * w + 1]);
+  const double ss = thi + tlo;
+  return 1.0 / sqrt(ss / (double)ncols + (double)eps);
+}
+
+__device__ __forceinline__ float z_value(float x, float w, double s) {
+  return (float)(((double)x * (double)w) * s);
+}
+
+// q8_1 of one 32-block held by 8 consecutive lanes (4 values each).  All 8 lanes of a group
+// must execute this together.  Returns the 4 int8 codes packed little-endian; the block
+// scale is returned through d_out (same value on all 8 lanes).
+__device__ __forceinline__ uint32_t quant_group(const float z[4], float &d_out) {
+  float amax = fmaxf(fmaxf(fabsf(z[0]), fabsf(z[1])), fmaxf(fabsf(z[2]), fabsf(z[3])));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const float d = amax / 127.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (int)roundf(z[i] * id);
+    packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * i);
+  }
+  d_out = d;
+  return packed;
+}
+
+__global__ __launch_bounds__(kThreads) void k_rms_norm(const float *__restrict__ x,
+                                                       const float *__restrict__ w,
+                                                       float *__restrict__ z, int ncols,
+                                                       float eps) {
+  __shared__ double red[2 * kThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const float *xr = x + row * ncols;
+  const double s = row_scale(xr, ncols, eps, red);
+  for (int j = threadIdx.x * 4; j < ncols; j += kColsPerPass) {
+    const float4 xv = *reinterpret_cast<const float4 *>(xr + j);
+    const float4 wv = *reinterpret_cast<const float4 *>(w + j);
+    float4 zv;
+    zv.x = z_value(xv.x, wv.x, s);
+    zv.y = z_value(xv.y, wv.y, s);
+    zv.z = z_value(xv.z, wv.z, s);
+    zv.w = z_value(xv.w, wv.w, s);
+    *reinterpret_cast<float4 *>(z + row * ncols + j) = zv;
+  }
+}
+
+// One workgroup per (1024-column slice, row).
+__global__ __launch_bounds__(kThreads) void k_quantize_q8_1(const float *__restrict__ z,
+                                                            int8_t *__restrict__ qs,
+                                                            float *__restrict__ d, int ncols) {
+  const int64_t row = blockIdx.y;
+  const int j = blockIdx.x * kColsPerPass + threadIdx.x * 4;
+  const bool live = j < ncols;  // whole 8-lane groups are live or not (ncols % 32 == 0)
+  float zv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const float4 v = *reinterpret_cast<const float4 *>(z + row * ncols + j);
+    zv[0] = v.x; zv[1] = v.y; zv[2] = v.z; zv[3] = v.w;
+  }
+  float db;
+  const uint32_t packed = quant_group(zv, db);
+  if (live) {
+    *reinterpret_cast<uint32_t *>(qs + row * ncols + j) = packed;
+    if ((threadIdx.x & 7) == 0) d[row * (ncols / 32) + j / 32] = db;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_rmsnorm_q8_1(const float *__restrict__ x,
+                                                           const float *__restrict__ w,
+                                                           float *__restrict__ z,
+                                                           int8_t *__restrict__ qs,
+                                                           float *__restrict__ d, int ncols,
+                                                           float eps) {
+  __shared__ double red[2 * kThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const float *xr = x + row * ncols;
+  const double s = row_scale(xr, ncols, eps, red);
+  for (int base = 0; base < ncols; base += kColsPerPass) {
+    const int j = base + threadIdx.x * 4;
+    const bool live = j < ncols;
+    float zv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const float4 xv = *reinterpret_cast<const float4 *>(xr + j);
+      const float4 wv = *reinterpret_cast<const float4 *>(w + j);
+      zv[0] = z_value(xv.x, wv.x, s);
+      zv[1] = z_value(xv.y, wv.y, s);
+      zv[2] = z_value(xv.z, wv.z, s);
+      zv[3] = z_value(xv.w, wv.w, s);
+      if (z != nullptr)
+        *reinterpret_cast<float4 *>(z + row * ncols + j) = make_float4(zv[0], zv[1], zv[2], zv[3]);
+    }
+    float db;
+    const uint32_t packed = quant_group(zv, db);
+    if (live) {
+      *reinterpret_cast<uint32_t *>(qs + row * ncols + j) = packed;
+      if ((threadIdx.x & 7) == 0) d[row * (ncols / 32) + j / 32] = db;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rms_norm(const float *x, const float *w, float *z, int ncols, int nrows,
+                           float eps, hipStream_t s) {
+  hipLaunchKernelGGL(k_rms_norm, dim3(nrows), dim3(kThreads), 0, s, x, w, z, ncols, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_q8_1(const float *z, int8_t *qs, float *d, int nrows, int ncols,
+                                hipStream_t s) {
+  const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
+  hipLaunchKernelGGL(k_quantize_q8_1, grid, dim3(kThreads), 0, s, z, qs, d, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d,
+                               int ncols, int nrows, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_q8_1, dim3(nrows), dim3(kThreads), 0, s, x, w, z, qs, d, ncols,
+                     eps);
+  return hipGetLastError();
+}
+
+}  // namespace fp8gemv

@@ -1,0 +1,143 @@
+/*
+ * fp8_gemv.h -- C ABI of the MI355X (gfx950) m=1 decode matvec library.
+ *
+ * The library implements the hot path of single-token decode described on the docs.rs source
+ * pages of memra-engine 0.125.0:
+ *   - a producer that RMS-normalises an activation row and quantises it to q8_1
+ *     (src/bin/q8_fuse_gate.rs: module doc, `run_shape`), and
+ *   - GEMVs that stream a weight matrix once from HBM against that q8_1 activation, for three
+ *     weight containers (src/bin/gemv_e4m3_bench.rs: module doc sections QUESTION,
+ *     THE COMPARISON and THE BLOCK-128 ARM; `synth_e4m3`, `synth_blk_grid`, `synth_q8_0`).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer on the current HIP device, owned by the caller; the
+ *     library never frees, retains or allocates memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the null
+ *     stream) and never synchronises.  Buffers must stay alive until the stream reaches the
+ *     launched work.
+ *   - Return value: 0 on success; a negative FP8GEMV_ERR_* code when the arguments are
+ *     invalid (checked on the host before anything is launched, so no GPU work is queued);
+ *     a positive value is the hipError_t reported by the launch.
+ *   - Sizes are elements unless named *_bytes.  Matrices are row-major.
+ *   - q8_1 activation = two planes: qs int8 [rows, cols] and d f32 [rows, cols/32] (one
+ *     scale per 32 consecutive values, d = amax/127; value = d * qs).  No per-block sum.
+ *   - Preconditions that are documented but not checked: no NaN/Inf in x, w, scales or grid;
+ *     no e4m3 NaN code (0x7F, 0xFF) in a weight plane (the bench page's generator excludes
+ *     it and says the real dispatch refuses it); buffers large enough for the sizes passed.
+ */
+#ifndef FP8_GEMV_H
+#define FP8_GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes (negative: argument errors found on the host, nothing launched). */
+#define FP8GEMV_OK              0
+#define FP8GEMV_ERR_NULL       (-1) /* a required pointer is NULL */
+#define FP8GEMV_ERR_SHAPE      (-2) /* cols/in_f not a positive multiple of 32, rows/m/out_f < 1 */
+#define FP8GEMV_ERR_ROW_BYTES  (-3) /* row_bytes below the container minimum */
+#define FP8GEMV_ERR_GRID       (-4) /* grid_cols != ceil(in_f / 128) */
+#define FP8GEMV_ERR_ALIGN      (-5) /* a pointer or row stride breaks the stated alignment */
+#define FP8GEMV_ERR_TOO_LARGE  (-6) /* a size beyond the stated limit */
+
+/* Limits.  in_f is bounded so that one activation row (staged in LDS) fits a workgroup;
+ * m is bounded by the launch grid's y dimension used for activation rows. */
+#define FP8GEMV_MAX_IN_F   65536
+#define FP8GEMV_MAX_M      65535
+
+/*
+ * rms_norm_f32 -- first half of the two-launch producer chain.
+ * Source: q8_fuse_gate.rs, module doc and `run_shape` (rms_norm(x, w, z, ncols, nrows, eps)).
+ * For each row r: z[r, j] = x[r, j] * w[j] / sqrt(mean_j(x[r, j]^2) + eps).
+ *   x    f32 [nrows, ncols]   input rows
+ *   w    f32 [ncols]          gain, broadcast over rows
+ *   z    f32 [nrows, ncols]   output (may not alias x or w)
+ *   ncols multiple of 32, <= FP8GEMV_MAX_IN_F; nrows >= 1; eps as given (1e-6 on the page)
+ * Arithmetic: the sum of squares is accumulated in double-double and rounded once to f64,
+ * s = 1 / sqrt(ss / ncols + eps) in f64, z = (float)((double)x * w * s).
+ * Alignment: x, w, z 16-byte aligned.
+ */
+int rms_norm_f32(const float *x, const float *w, float *z, int ncols, int nrows, float eps,
+                 void *stream);
+
+/*
+ * quantize_q8_1 -- second half of the chain; also the x -> q8_1 step in front of each GEMV.
+ * Source: q8_fuse_gate.rs, module doc (int8 qs plus one f32 scale per 32 values) and the note
+ * on the `id = 1/d` branch; gemv_e4m3_bench.rs, THE COMPARISON (the f32 activation is
+ * quantised to q8_1 before the matvec).
+ * Per 32-block, all in f32: amax = max|z|, d = amax / 127, id = (d != 0) ? 1 / d : 0,
+ * qs = round(z * id) with halves away from zero.
+ *   z   f32 [nrows, ncols]      input
+ *   qs  int8 [nrows, ncols]     output
+ *   d   f32 [nrows, ncols / 32] output
+ * Argument order follows the page (nrows before ncols).  Alignment: z, qs, d 16-byte aligned.
+ */
+int quantize_q8_1(const float *z, int8_t *qs, float *d, int nrows, int ncols, void *stream);
+
+/*
+ * rmsnorm_q8_1 -- the fused producer: rms_norm_f32 then quantize_q8_1 in one launch.
+ * Source: q8_fuse_gate.rs, module doc (`rms_norm_zq8_f32`: one launch, still writes z, and
+ * must be byte-identical in z, qs and d to the two-launch chain).
+ * Same arguments and results as the chain; z may be NULL, in which case z is not stored
+ * (qs and d are unchanged).  The bytes written are identical to rms_norm_f32 followed by
+ * quantize_q8_1 on the same inputs.
+ */
+int rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d, int ncols,
+                 int nrows, float eps, void *stream);
+
+/*
+ * gemv_q8_0_q81 -- matvec over ggml Q8_0 weight rows.
+ * Source: gemv_e4m3_bench.rs, QUESTION and THE COMPARISON (arm Q8_0: 34 bytes per 32
+ * weights, an fp16 scale then 32 int8, row_bytes = in_f / 32 * 34) and `synth_q8_0`.
+ * y[t, r] = sum_b fp16(W[r].blk[b].d) * d_a[t, b] * sum_{i<32} W[r].blk[b].qs[i] * qs[t, 32b+i]
+ *   W          [out_f] rows of row_bytes bytes; each row starts with in_f/32 blocks of 34 B
+ *              (little-endian fp16 scale at bytes 0..1, then 32 int8)
+ *   row_bytes  >= in_f / 32 * 34, even
+ *   qs, d      q8_1 activation rows [m, in_f] / [m, in_f / 32]
+ *   y          f32 [m, out_f]
+ * Alignment: W and row_bytes 2-byte aligned; the fast path also needs W 16-byte aligned,
+ * row_bytes % 16 == 0 and in_f % 256 == 0, otherwise a slower path runs.  qs, d 16-byte
+ * aligned.  Each activation row is computed independently: row t of an m-row call is
+ * bit-identical to an m=1 call on that row.
+ */
+int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
+                  int m, int in_f, int out_f, void *stream);
+
+/*
+ * gemv_e4m3_q81 -- matvec over raw OCP FP8 E4M3 weights with one per-tensor f32 scale.
+ * Source: gemv_e4m3_bench.rs, THE COMPARISON (arm E4M3: the raw checkpoint bytes are the
+ * weight stream, row_bytes == in_f, no dequantisation) and `synth_e4m3`.
+ * y[t, r] = scale * sum_k e4m3(W[r, k]) * d_a[t, k/32] * qs[t, k]
+ *   W          u8 [out_f] rows of row_bytes bytes (first in_f bytes used)
+ *   row_bytes  >= in_f, multiple of 16;  W 16-byte aligned
+ *   scale      per-tensor dequantisation factor, applied once per output
+ *   qs, d, y   as for gemv_q8_0_q81
+ */
+int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
+                  const float *d, float *y, int m, int in_f, int out_f, void *stream);
+
+/*
+ * gemv_e4m3_blk128_q81 -- matvec over raw e4m3 weights with a block-128 f32 scale grid.
+ * Source: gemv_e4m3_bench.rs, THE BLOCK-128 ARM (an f32 [ceil(out_f/128), ceil(in_f/128)]
+ * grid, the weight_scale_inv of weight_block_size [128, 128] checkpoints) and
+ * `synth_blk_grid`.
+ * y[t, r] = sum_k grid[r/128, k/128] * e4m3(W[r, k]) * d_a[t, k/32] * qs[t, k]
+ *   grid       f32 [ceil(out_f/128), grid_cols], row-major, a multiplier
+ *   grid_cols  must equal ceil(in_f / 128)
+ *   other arguments as for gemv_e4m3_q81
+ */
+int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid, int grid_cols,
+                         const int8_t *qs, const float *d, float *y, int m, int in_f, int out_f,
+                         void *stream);
+
+/* Human-readable text for a return code (static storage, never NULL). */
+const char *fp8gemv_strerror(int rc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_GEMV_H */

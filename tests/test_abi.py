@@ -1,0 +1,137 @@
+"""The C ABI library on the host: it loads, exports every declared entry point, and rejects
+bad arguments with the documented codes before anything reaches the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8_gemv.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def _codes():
+    src = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(FP8GEMV_\w+)\s+\(?(-?\d+)\)?", src)}
+
+
+@pytest.fixture(scope="module")
+def fg():
+    import fp8_gemv_amd
+    return fp8_gemv_amd
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1",
+                                  "gemv_q8_0_q81", "gemv_e4m3_q81", "gemv_e4m3_blk128_q81",
+                                  "fp8gemv_strerror"])
+
+
+def test_library_exports_every_declared_symbol(fg):
+    out = subprocess.run(["nm", "-D", "--defined-only", fg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(fg.lib(), name)
+    assert set(fg.EXPORTS) == set(_declared())
+
+
+def test_library_is_built_for_gfx950_only(fg):
+    blob = open(fg.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_python_constants_match_header(fg):
+    codes = _codes()
+    for k, v in codes.items():
+        assert getattr(fg, k) == v, k
+
+
+def test_strerror(fg):
+    assert fg.strerror(0) == "ok"
+    for code in (-1, -2, -3, -4, -5, -6):
+        assert fg.strerror(code) and fg.strerror(code) != "unknown error"
+    assert fg.strerror(-99) == "unknown error"
+
+
+# Argument checks run on the host and return before any HIP call, so they can be exercised
+# here with fake (never dereferenced) addresses.
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def test_producer_argument_errors(fg):
+    L = fg.lib()
+    assert L.rms_norm_f32(None, FAKE, FAKE, 64, 1, 1e-6, None) == fg.FP8GEMV_ERR_NULL
+    assert L.rms_norm_f32(FAKE, FAKE, FAKE, 48, 1, 1e-6, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.rms_norm_f32(FAKE, FAKE, FAKE, 0, 1, 1e-6, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.rms_norm_f32(FAKE, FAKE, FAKE, 64, 0, 1e-6, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.rms_norm_f32(FAKE, FAKE, FAKE, 65536 + 32, 1, 1e-6, None) == fg.FP8GEMV_ERR_TOO_LARGE
+    assert L.rms_norm_f32(FAKE + 4, FAKE, FAKE, 64, 1, 1e-6, None) == fg.FP8GEMV_ERR_ALIGN
+    assert L.quantize_q8_1(FAKE, None, FAKE, 1, 64, None) == fg.FP8GEMV_ERR_NULL
+    assert L.quantize_q8_1(FAKE, FAKE, FAKE, 1, 40, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.quantize_q8_1(FAKE, FAKE, FAKE, 70000, 64, None) == fg.FP8GEMV_ERR_TOO_LARGE
+    assert L.quantize_q8_1(FAKE, FAKE + 8, FAKE, 1, 64, None) == fg.FP8GEMV_ERR_ALIGN
+    assert L.rmsnorm_q8_1(FAKE, FAKE, None, None, FAKE, 64, 1, 1e-6, None) == fg.FP8GEMV_ERR_NULL
+    assert L.rmsnorm_q8_1(FAKE, FAKE, None, FAKE, FAKE, 33, 1, 1e-6, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.rmsnorm_q8_1(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 64, 1, 1e-6, None) == fg.FP8GEMV_ERR_ALIGN
+
+
+def test_gemv_argument_errors(fg):
+    L = fg.lib()
+    e = fg
+    # NULL pointers
+    assert L.gemv_e4m3_q81(None, 64, 1.0, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_NULL
+    assert L.gemv_q8_0_q81(FAKE, 68, FAKE, FAKE, None, 1, 64, 8, None) == e.FP8GEMV_ERR_NULL
+    assert L.gemv_e4m3_blk128_q81(FAKE, 64, None, 1, FAKE, FAKE, FAKE, 1, 64, 8,
+                                  None) == e.FP8GEMV_ERR_NULL
+    # shapes
+    assert L.gemv_e4m3_q81(FAKE, 64, 1.0, FAKE, FAKE, FAKE, 0, 64, 8, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.gemv_e4m3_q81(FAKE, 64, 1.0, FAKE, FAKE, FAKE, 1, 48, 8, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.gemv_e4m3_q81(FAKE, 64, 1.0, FAKE, FAKE, FAKE, 1, 64, 0, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.gemv_q8_0_q81(FAKE, 68, FAKE, FAKE, FAKE, 1, 16, 8, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.gemv_e4m3_q81(FAKE, 2 ** 17 + 32, 1.0, FAKE, FAKE, FAKE, 1, 2 ** 17, 8,
+                           None) == e.FP8GEMV_ERR_TOO_LARGE
+    assert L.gemv_e4m3_q81(FAKE, 64, 1.0, FAKE, FAKE, FAKE, 70000, 64, 8,
+                           None) == e.FP8GEMV_ERR_TOO_LARGE
+    # row_bytes below the container minimum
+    assert L.gemv_e4m3_q81(FAKE, 48, 1.0, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ROW_BYTES
+    assert L.gemv_q8_0_q81(FAKE, 66, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ROW_BYTES
+    # grid columns
+    assert L.gemv_e4m3_blk128_q81(FAKE, 256, FAKE, 1, FAKE, FAKE, FAKE, 1, 256, 8,
+                                  None) == e.FP8GEMV_ERR_GRID
+    # alignment
+    assert L.gemv_e4m3_q81(FAKE + 8, 64, 1.0, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gemv_e4m3_q81(FAKE, 72, 1.0, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gemv_q8_0_q81(FAKE + 1, 68, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gemv_q8_0_q81(FAKE, 69, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gemv_q8_0_q81(FAKE, 68, FAKE + 4, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+
+
+def test_binding_rejects_cpu_tensors_and_short_buffers(fg):
+    import torch
+    x = torch.zeros(64)
+    with pytest.raises(ValueError):
+        fg.rms_norm_f32(x, x, x, 64, 1)
+
+
+def test_byte_counts_match_the_pages(fg):
+    # gemv_e4m3_bench.rs, QUESTION: Q8_0 is 34 B per 32 weights = 1.0625 B/weight, e4m3 is
+    # exactly 1 B/weight (a 5.88% smaller stream).
+    for out_f, in_f in [(5120, 5120), (17408, 5120), (5120, 17408), (2048, 2048), (3, 96)]:
+        q, e = fg.q8_0_weight_bytes(out_f, in_f), fg.e4m3_weight_bytes(out_f, in_f)
+        assert q * 32 == e * 34 and q / e == 1.0625
+        assert abs((1 - e / q) - 0.0588) < 5e-4
+    # THE BLOCK-128 ARM: the grid is "~21 KB" and "0.02%" of the weight bytes for the widest
+    # 27B projection; exactly 136 x 40 f32 = 21,760 B = 0.0244%.
+    g = fg.blk128_grid_bytes(17408, 5120)
+    assert g == 21760 and g == fg.blk128_grid_bytes(5120, 17408)
+    assert round(100 * g / fg.e4m3_weight_bytes(17408, 5120), 2) == 0.02

@@ -1,0 +1,214 @@
+"""GPU parity of the three GEMVs (gemv_e4m3_bench.rs: THE COMPARISON, THE BLOCK-128 ARM)
+against the CPU oracle: |y_gpu - y| <= 1e-5 * sum_k |term_k| per output, on the same seeded
+inputs, from one-tile shapes with ragged tails up to the 27B-class projection shapes run in
+the launch configuration the bench times."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import case, dev, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+KINDS = ["q8_0", "e4m3", "blk128"]
+SCALE = 2.0 ** -4  # the per-tensor scale of the e4m3 configs
+
+
+@pytest.fixture(scope="module")
+def fg():
+    import fp8_gemv_amd
+    return fp8_gemv_amd
+
+
+class Case:
+    """Weights of one container plus a q8_1 activation, on host and device."""
+
+    def __init__(self, kind, out_f, in_f, m, seed=0):
+        self.kind, self.out_f, self.in_f, self.m = kind, out_f, in_f, m
+        if kind == "q8_0":
+            self.W = synth.q8_0_weights(out_f, in_f)
+        else:
+            self.W = synth.e4m3_weights(out_f, in_f)
+        self.row_bytes = self.W.shape[1]
+        self.grid = synth.blk128_grid(out_f, in_f) if kind == "blk128" else None
+        x = synth.x_rows(in_f, m)
+        if seed:
+            x = np.stack([synth.f32(seed + t, in_f) for t in range(m)])
+        self.qs, self.d = oracle.quantize_q8_1(x)
+        self.Wd = to_dev(self.W)
+        self.gd = to_dev(self.grid) if self.grid is not None else None
+
+    def gpu(self, fg, qs=None, d=None, m=None, Wd=None, row_bytes=None):
+        m = self.m if m is None else m
+        qs = to_dev(self.qs) if qs is None else qs
+        d = to_dev(self.d) if d is None else d
+        Wd = self.Wd if Wd is None else Wd
+        rb = self.row_bytes if row_bytes is None else row_bytes
+        y = torch.full((m, self.out_f), float("nan"), device=dev())
+        if self.kind == "q8_0":
+            fg.gemv_q8_0_q81(Wd, rb, qs, d, y, m, self.in_f, self.out_f)
+        elif self.kind == "e4m3":
+            fg.gemv_e4m3_q81(Wd, rb, SCALE, qs, d, y, m, self.in_f, self.out_f)
+        else:
+            fg.gemv_e4m3_blk128_q81(Wd, rb, self.gd, self.grid.shape[1], qs, d, y, m,
+                                    self.in_f, self.out_f)
+        return host(y)
+
+    def oracle(self, rows=None):
+        if self.kind == "q8_0":
+            return oracle.gemv_q8_0(self.W, self.row_bytes, self.qs, self.d, self.in_f,
+                                    self.out_f, rows)
+        if self.kind == "e4m3":
+            return oracle.gemv_e4m3(self.W, self.row_bytes, SCALE, self.qs, self.d, self.in_f,
+                                    self.out_f, rows)
+        return oracle.gemv_e4m3_blk128(self.W, self.row_bytes, self.grid, self.qs, self.d,
+                                       self.in_f, self.out_f, rows)
+
+
+def _assert_close(y, yo, A, rows=None):
+    if rows is not None:
+        y, yo, A = y[:, rows[0]:rows[1]], yo[:, rows[0]:rows[1]], A[:, rows[0]:rows[1]]
+    err = np.abs(y.astype(np.float64) - yo)
+    bad = ~(err <= TOL * A)
+    assert not bad.any(), f"{bad.sum()} outputs off; worst rel {np.max(err / A):.3e}"
+
+
+# Shapes [out_f, in_f] from a single window to several, with ragged tails in both directions
+# (in_f not a multiple of the 1 KiB window or of 256, out_f not a multiple of the 8 rows per
+# workgroup or of the 128-row grid tile).
+SMALL = [(1, 32), (7, 96), (130, 160), (131, 288), (257, 1056), (300, 2080), (64, 4096),
+         (129, 4352), (33, 1280), (250, 2048)]
+
+
+@pytest.mark.parametrize("m", [1, 3])
+@pytest.mark.parametrize("out_f,in_f", SMALL)
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_small_shapes_match_oracle(fg, kind, out_f, in_f, m):
+    case(f"{kind} out_f={out_f} in_f={in_f} m={m}")
+    c = Case(kind, out_f, in_f, m)
+    y = c.gpu(fg)
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+
+
+# The 27B-class projection shapes of the bench, m = 1, the same launch as bench.py; outputs
+# sampled in three row ranges (start, middle, end) that the oracle computes exactly.
+FULL = [(5120, 5120), (17408, 5120), (5120, 17408)]
+
+
+@pytest.mark.parametrize("out_f,in_f", FULL)
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_full_shapes_sampled_rows(fg, kind, out_f, in_f):
+    case(f"{kind} full out_f={out_f} in_f={in_f}")
+    c = Case(kind, out_f, in_f, 1)
+    y = c.gpu(fg)
+    assert np.all(np.isfinite(y))
+    for r0 in (0, out_f // 2 - 37, out_f - 96):
+        rows = (r0, r0 + 96)
+        yo, A = c.oracle(rows)
+        _assert_close(y, yo, A, rows)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_m_rows_bit_identical_to_m1(fg, kind):
+    out_f, in_f = 17408, 5120
+    c = Case(kind, out_f, in_f, 8)
+    for m in (1, 2, 4, 8):
+        case(f"{kind} m={m} out_f={out_f} in_f={in_f}")
+        y = c.gpu(fg, qs=to_dev(c.qs[:m]), d=to_dev(c.d[:m]), m=m)
+        for t in range(m):
+            y1 = c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)
+            assert y[t].tobytes() == y1[0].tobytes(), (m, t)
+    yo, A = c.oracle((1000, 1100))
+    _assert_close(y, yo, A, (1000, 1100))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_rotated_copies_are_identical(fg, kind):
+    case(f"{kind} rotated copies")
+    c = Case(kind, 5120, 5120, 1)
+    ys = [c.gpu(fg, Wd=to_dev(c.W)).tobytes() for _ in range(3)]
+    assert ys[0] == ys[1] == ys[2]
+
+
+def test_e4m3_decode_on_device_exhaustive(fg):
+    # Row r holds code r (0x7F / 0xFF excluded) in column 0 and zeros elsewhere; a one-hot
+    # activation with d = 1 reads that column, so y[r] is the decoded code exactly.
+    case("e4m3 decode through gemv_e4m3_q81 / blk128")
+    codes = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    in_f = 32
+    W = np.zeros((len(codes), in_f), dtype=np.uint8)
+    W[:, 0] = codes
+    qs = np.zeros((1, in_f), dtype=np.int8)
+    qs[0, 0] = 1
+    d = np.ones((1, 1), dtype=np.float32)
+    y = torch.empty((1, len(codes)), device=dev())
+    fg.gemv_e4m3_q81(to_dev(W), in_f, 1.0, to_dev(qs), to_dev(d), y, 1, in_f, len(codes))
+    want = np.array([oracle.e4m3_value(c) for c in codes])
+    assert np.array_equal(host(y)[0].astype(np.float64), want)
+    grid = np.ones(((len(codes) + 127) // 128, 1), dtype=np.float32)
+    fg.gemv_e4m3_blk128_q81(to_dev(W), in_f, to_dev(grid), 1, to_dev(qs), to_dev(d), y, 1, in_f,
+                            len(codes))
+    assert np.array_equal(host(y)[0].astype(np.float64), want)
+
+
+@pytest.mark.parametrize("in_f", [2048, 288])
+def test_q8_0_unaligned_rows_take_the_generic_path(fg, in_f):
+    # W 2-byte aligned but not 16-byte aligned (and in_f % 256 != 0 for 288): generic path.
+    case(f"q8_0 generic path in_f={in_f}")
+    c = Case("q8_0", 77, in_f, 2)
+    flat = np.zeros(c.W.size + 16, dtype=np.uint8)
+    flat[2:2 + c.W.size] = c.W.reshape(-1)
+    buf = to_dev(flat)
+    y = c.gpu(fg, Wd=buf[2:])
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+    assert y.tobytes() == c.gpu(fg, Wd=buf[2:]).tobytes()
+
+
+@pytest.mark.parametrize("kind", ["e4m3", "blk128", "q8_0"])
+def test_padded_row_stride(fg, kind):
+    case(f"{kind} padded row stride")
+    out_f, in_f = 100, 1024
+    c = Case(kind, out_f, in_f, 1)
+    pad = 48
+    Wp = np.zeros((out_f, c.row_bytes + pad), dtype=np.uint8)
+    Wp[:, :c.row_bytes] = c.W
+    Wp[:, c.row_bytes:] = 0x7F  # never read
+    y = c.gpu(fg, Wd=to_dev(Wp), row_bytes=c.row_bytes + pad)
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_max_in_f(fg, kind):
+    case(f"{kind} in_f=65536")
+    c = Case(kind, 40, 65536, 1)
+    y = c.gpu(fg)
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+
+
+def test_bad_arguments_raise_and_launch_nothing(fg):
+    case("argument errors through the binding")
+    c = Case("e4m3", 64, 256, 1)
+    y = torch.zeros((1, 64), device=dev())
+    with pytest.raises(fg.Fp8GemvError) as e:
+        fg.gemv_e4m3_q81(c.Wd, 128, 1.0, to_dev(c.qs), to_dev(c.d), y, 1, 256, 64)
+    assert e.value.rc == fg.FP8GEMV_ERR_ROW_BYTES
+    with pytest.raises(fg.Fp8GemvError):
+        fg.gemv_e4m3_blk128_q81(c.Wd, 256, to_dev(np.ones((1, 5), np.float32)), 5,
+                                to_dev(c.qs), to_dev(c.d), y, 1, 256, 64)
+    assert np.all(host(y) == 0)
+
+
+def test_one_hip_runtime_in_process(fg):
+    torch.zeros(1, device=dev())
+    maps = open(f"/proc/{os.getpid()}/maps").read().splitlines()
+    libs = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(libs) == 1, libs
