@@ -193,40 +193,52 @@ def main() -> int:
                 qs, d = producer((out_f, in_f))
                 arm_objs[(out_f, in_f, a)].launch(qs, d)
 
+    def timed(fn, n_inner):
+        """Run fn once between HIP events on the launch stream; returns ms per inner unit."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_inner
+
+    def capture(fn):
+        """Capture fn's launches into a HIP graph (torch's stream capture)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+    log(f"warmup {args.warmup} eager steps done")
 
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # Eager steps: one host launch per kernel (bound by host launch rate, kept for reference).
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    eager_ms = timed(lambda: [step() for _ in range(args.steps)], args.steps)
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # The timed region: K steps captured once as a HIP graph, replayed after one untimed replay.
+    graph = capture(lambda: [step() for _ in range(args.steps)])
+    graph.replay()
+    torch.cuda.synchronize()
+    ms_per_step = timed(graph.replay, args.steps)
     step_wbytes = sum(weight_bytes(a, o, i) for (o, i, a) in arm_objs)
     value = step_wbytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step:.3f} ms (host wall {wall_ms:.3f} ms), {value:.1f} GB/s of weights")
+    log(f"step {ms_per_step:.4f} ms (graph), eager {eager_ms:.4f} ms, {value:.1f} GB/s of weights")
 
-    # Per-kernel timing: back-to-back launches of one GEMV over its rotated copies, bracketed
-    # by HIP events on the launch stream; the q8_1 activation is produced once before.
+    # Per-kernel timing: one GEMV launched back to back over its rotated copies, captured as a
+    # graph and bracketed by HIP events on the launch stream; q8_1 produced once before.
     detail = {}
     for (out_f, in_f, a), obj in arm_objs.items():
         qs, d = producer((out_f, in_f))
-        for _ in range(min(obj.copies, 4)):
-            obj.launch(qs, d)
         n = max(args.kernel_iters, obj.copies)
-        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        k0.record(stream)
-        for _ in range(n):
-            obj.launch(qs, d)
-        k1.record(stream)
-        torch.cuda.synchronize()
-        us = k0.elapsed_time(k1) * 1e3 / n
+        g = capture(lambda: [obj.launch(qs, d) for _ in range(n)])
+        g.replay()
+        us = timed(g.replay, n) * 1e3
         wb = weight_bytes(a, out_f, in_f)
         detail[f"{a}@{out_f}x{in_f}"] = {
             "us": round(us, 3), "weight_GBs": round(wb / us / 1e3, 1),
@@ -235,9 +247,10 @@ def main() -> int:
         log(f"{a:7s} {out_f}x{in_f}: {us:8.2f} us  {wb / us / 1e3:7.1f} GB/s")
         if args.jsonl:
             with open(args.jsonl, "a") as f:
-                f.write(json.dumps({"arm": a, "out_f": out_f, "in_f": in_f, **detail[f"{a}@{out_f}x{in_f}"]}) + "\n")
+                f.write(json.dumps({"arm": a, "out_f": out_f, "in_f": in_f,
+                                    **detail[f"{a}@{out_f}x{in_f}"]}) + "\n")
 
-    # Producer alone (latency-bound; the gate page's site widths).
+    # Producer alone (latency-bound; the gate page's site widths), fused vs two-launch chain.
     prod_us = {}
     for ncols in (1536, 4096, 8192):
         x = torch.from_numpy(synth.x_rows(ncols, 1)).to(dev)
@@ -252,15 +265,10 @@ def main() -> int:
                 else:
                     fg.rms_norm_f32(x, w, z, ncols, 1, EPS)
                     fg.quantize_q8_1(z, qs, d, 1, ncols)
-            for _ in range(3):
-                run()
-            k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            k0.record(stream)
-            for _ in range(50):
-                run()
-            k1.record(stream)
-            torch.cuda.synchronize()
-            prod_us[f"{variant}@{ncols}"] = round(k0.elapsed_time(k1) * 1e3 / 50, 3)
+            run()
+            g = capture(lambda: [run() for _ in range(50)])
+            g.replay()
+            prod_us[f"{variant}@{ncols}"] = round(timed(g.replay, 50) * 1e3, 3)
 
     # Roofline of the dominant GEMV kernel (largest time per step).
     dom_key = max(detail, key=lambda k: detail[k]["us"])
@@ -288,7 +296,7 @@ def main() -> int:
                    "m": 1, "shapes": [f"{o}x{i}" for o, i in shapes], "arms": arms,
                    "eps": EPS, "e4m3_scale": SCALE},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "host_wall_ms_per_step": round(wall_ms, 4),
+        "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
         "gemv": detail, "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -8,20 +8,26 @@
 //
 // gfx950 design (the page's kernel is a warp-per-row CUDA MMVQ doing cvt + fmaf; this one is
 // not a translation of it):
-//   * A workgroup is 4 wave64s; each wave owns RPW consecutive weight rows.  A "window" is
+//   * A workgroup is WAVES wave64s; each wave owns RPW consecutive weight rows.  A "window" is
 //     1024 consecutive columns: lane l streams bytes [16l, 16l+16) of the window with one
 //     16-byte non-temporal load per row, so every wave-wide load instruction reads 1 KiB of
-//     contiguous HBM and every weight byte is fetched exactly once.
-//   * U windows x RPW rows of loads are issued before any of them is consumed, so each lane
-//     keeps U*RPW 16-byte loads in flight.
-//   * The q8_1 activation row is staged once per workgroup in LDS as f16 (int8 values are
-//     exact in f16) plus its f32 block scales, zero-padded to whole windows.
+//     contiguous HBM and every weight byte is fetched exactly once.  U windows x RPW rows of
+//     loads are in flight per lane before any is consumed.
+//   * Order of memory operations at kernel start: first the few activation loads this thread
+//     stages, then the weight loads.  Loads of one wave complete in issue order, so staging
+//     (which waits only for the older activation loads) overlaps the weight stream instead of
+//     waiting behind it.
+//   * The q8_1 activation row is staged once per workgroup in LDS as f16 (int8 is exact in
+//     f16, converted with the 0x6400 exponent trick) next to its block scales -- for the
+//     block-128 container the scale already times the grid value of the workgroup's
+//     128-row tile (all rows of a workgroup lie in one tile).
 //   * Decode: v_cvt_scalef32_pk_f16_fp8 turns two e4m3 bytes into two f16 with scale 1.0
 //     (every e4m3 value, subnormals included, is exact in f16); v_dot2_f32_f16 multiplies a
 //     weight pair by an activation pair and accumulates in f32 (each product is exact: 4 + 8
-//     significant bits).  One lane's 16 columns lie in one q8_1 block and one 128-column
-//     grid tile, so its 16-term partial is scaled once by the block scale (times the grid
-//     value for block-128).
+//     significant bits).  A lane's 16 columns lie in one q8_1 block and one 128-column tile,
+//     so its 16-term partial is scaled once.
+//   * At most 64 VGPRs (8 waves per SIMD): on this part occupancy, not arithmetic, decides
+//     how close the stream gets to the HBM roofline.
 //   * Each row's 64 lane partials are summed with a DPP butterfly + fixed-order readlanes.
 // Activation rows t = blockIdx.y are independent and run identical code, so row t of an
 // m-row call is bit-identical to an m=1 call on that row.
@@ -30,38 +36,24 @@
 namespace fp8gemv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kWinCols = kWave * 16;  // 1024 columns per window
 
 __host__ __device__ constexpr int num_windows(int in_f) { return (in_f + kWinCols - 1) / kWinCols; }
 
-// Bytes of LDS for one staged activation row: f16 values then f32 block scales.
+// LDS bytes for one staged activation row: f16 values then f32 block scales, whole windows.
 __host__ __device__ constexpr size_t act_lds_bytes(int in_f) {
   return (size_t)num_windows(in_f) * (kWinCols * 2 + (kWinCols / 32) * 4);
 }
 
-// Stage q8_1 row t into LDS: f16 qs for columns [0, nwin*1024) and f32 d for blocks
-// [0, nwin*32); entries past in_f are zero.
-__device__ __forceinline__ void stage_activation(const int8_t *__restrict__ qs,
-                                                 const float *__restrict__ d, int in_f,
-                                                 _Float16 *act, float *dsc) {
-  const int nwin = num_windows(in_f);
-  const int ncols = nwin * kWinCols;
-  for (int c = threadIdx.x * 16; c < ncols; c += kThreads * 16) {
-    int4_t q = {0, 0, 0, 0};
-    if (c < in_f) q = *reinterpret_cast<const int4_t *>(qs + c);
-    _Float16 h[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) h[4 * j + b] = (_Float16)(int)(int8_t)(q[j] >> (8 * b));
-    }
-    *reinterpret_cast<int4_t *>(act + c) = *reinterpret_cast<const int4_t *>(h);
-    *reinterpret_cast<int4_t *>(act + c + 8) = *reinterpret_cast<const int4_t *>(h + 8);
-  }
-  const int nb = in_f / 32;
-  for (int b = threadIdx.x; b < nwin * (kWinCols / 32); b += kThreads) dsc[b] = (b < nb) ? d[b] : 0.0f;
+// int8 x4 -> two f16 pairs, exactly: after flipping the sign bit a byte u is 0..255 and the
+// f16 with bits 0x6400 | u is 1024 + u; subtracting 1152 leaves the signed value.
+__device__ __forceinline__ void i8x4_to_f16(uint32_t q, half2_t &lo, half2_t &hi) {
+  const uint32_t u = q ^ 0x80808080u;
+  const uint32_t a = (u & 0xFFu) | ((u & 0xFF00u) << 8) | 0x64006400u;
+  const uint32_t b = ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u;
+  const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(half2_t, a) - off;
+  hi = __builtin_bit_cast(half2_t, b) - off;
 }
 
 // 16-term dot of one lane's 16 e4m3 weights (one 16-byte load) with 16 staged f16 values.
@@ -77,11 +69,21 @@ __device__ __forceinline__ float dot16(const int4_t w, const half2_t a[8]) {
   return p;
 }
 
-template <bool BLK, int RPW, int U>
-__global__ __launch_bounds__(kThreads) void k_gemv_e4m3(
-    const uint8_t *__restrict__ W, int64_t row_bytes, float scale, const float *__restrict__ grid,
-    int grid_cols, const int8_t *__restrict__ qs, const float *__restrict__ d,
-    float *__restrict__ y, int in_f, int out_f) {
+// Launch shape.  K chunks of 16 activation columns and KD block scales per thread cover the
+// whole activation row: K * WAVES * 1024 >= in_f and KD * WAVES * 64 >= in_f / 32.
+template <int WAVES_, int RPW_, int U_, int K_, int KD_>
+struct Cfg {
+  static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, K = K_, KD = KD_;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int MAX_IN_F = K * THREADS * 16;
+};
+
+template <bool BLK, class C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
+                 const float *__restrict__ grid, int grid_cols, const int8_t *__restrict__ qs,
+                 const float *__restrict__ d, float *__restrict__ y, int in_f, int out_f) {
+  constexpr int RPW = C::RPW, U = C::U, K = C::K, KD = C::KD, NTH = C::THREADS;
   extern __shared__ __align__(16) unsigned char lds[];
   const int nwin = num_windows(in_f);
   _Float16 *act = reinterpret_cast<_Float16 *>(lds);
@@ -90,8 +92,32 @@ __global__ __launch_bounds__(kThreads) void k_gemv_e4m3(
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int rbase = (blockIdx.x * kWaves + wave) * RPW;
+  const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
+  const int8_t *qa = qs + (int64_t)t * in_f;
+  const float *da = d + (int64_t)t * (in_f / 32);
 
+  // 1. this thread's share of the activation row (oldest loads).
+  int4_t aq[K];
+  float dv[KD];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int c = (threadIdx.x + k * NTH) * 16;
+    aq[k] = (int4_t){0, 0, 0, 0};
+    if (c < in_f) aq[k] = *reinterpret_cast<const int4_t *>(qa + c);
+  }
+  // Grid row of this workgroup (its rows all lie in one 128-row tile); clamped so a
+  // workgroup past the last row still reads inside the grid.
+  const int rfirst = blockIdx.x * C::WAVES * RPW;
+  const float *grow =
+      BLK ? grid + (int64_t)((rfirst < out_f ? rfirst : out_f - 1) / 128) * grid_cols : nullptr;
+#pragma unroll
+  for (int k = 0; k < KD; ++k) {
+    const int b = threadIdx.x + k * NTH;
+    dv[k] = 0.0f;
+    if (b < in_f / 32) dv[k] = BLK ? da[b] * grow[b / 4] : da[b];
+  }
+
+  // 2. the first batch of weight loads.
   const uint8_t *wrow[RPW];
   bool rok[RPW];
 #pragma unroll
@@ -99,13 +125,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_e4m3(
     rok[r] = rbase + r < out_f;
     wrow[r] = W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + lane * 16;
   }
-  // Grid row of this wave's rows (RPW divides 128, so all of them share it); clamped so a wave
-  // past the last row still reads inside the grid.
-  const float *grow =
-      BLK ? grid + (int64_t)((rbase < out_f ? rbase : out_f - 1) / 128) * grid_cols : nullptr;
-
-  // Issue the first batch of weight loads before staging the activation so that HBM traffic
-  // starts immediately.
   int4_t wv[U][RPW];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -117,13 +136,29 @@ __global__ __launch_bounds__(kThreads) void k_gemv_e4m3(
     }
   }
 
-  stage_activation(qs + (int64_t)t * in_f, d + (int64_t)t * (in_f / 32), in_f, act, dsc);
+  // 3. stage the activation (f16) and its scales in LDS; zero past in_f.
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int c = (threadIdx.x + k * NTH) * 16;
+    if (c < nwin * kWinCols) {
+      half2_t h[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) i8x4_to_f16((uint32_t)aq[k][j], h[2 * j], h[2 * j + 1]);
+      *reinterpret_cast<int4_t *>(act + c) = *reinterpret_cast<const int4_t *>(h);
+      *reinterpret_cast<int4_t *>(act + c + 8) = *reinterpret_cast<const int4_t *>(h + 4);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KD; ++k) {
+    const int b = threadIdx.x + k * NTH;
+    if (b < nwin * (kWinCols / 32)) dsc[b] = dv[k];
+  }
   __syncthreads();
 
+  // 4. stream.
   float acc[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-
   for (int w0 = 0; w0 < nwin; w0 += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -133,13 +168,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv_e4m3(
         half2_t a[8];
         *reinterpret_cast<int4_t *>(a) = *reinterpret_cast<const int4_t *>(act + col);
         *reinterpret_cast<int4_t *>(a + 4) = *reinterpret_cast<const int4_t *>(act + col + 8);
-        float sc = dsc[col / 32];
-        if (BLK) sc *= (col < in_f) ? grow[col / 128] : 0.0f;
+        const float sc = dsc[col / 32];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) acc[r] = fmaf(dot16(wv[u][r], a), sc, acc[r]);
       }
     }
-    // Next batch.
     const int nxt = w0 + U;
     if (nxt < nwin) {
 #pragma unroll
@@ -148,7 +181,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_e4m3(
         for (int r = 0; r < RPW; ++r) {
           const int col = (nxt + u) * kWinCols + lane * 16;
           wv[u][r] = (int4_t){0, 0, 0, 0};
-          if (rok[r] && col < in_f) wv[u][r] = load_stream16(wrow[r] + (int64_t)(nxt + u) * kWinCols);
+          if (rok[r] && col < in_f)
+            wv[u][r] = load_stream16(wrow[r] + (int64_t)(nxt + u) * kWinCols);
         }
       }
     }
@@ -161,25 +195,48 @@ __global__ __launch_bounds__(kThreads) void k_gemv_e4m3(
   }
 }
 
-template <bool BLK, int RPW, int U>
+template <bool BLK, class C>
 hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                       int grid_cols, const int8_t *qs, const float *d, float *y, int m,
                       int in_f, int out_f, hipStream_t s) {
-  const size_t lds = act_lds_bytes(in_f);
-  auto kern = k_gemv_e4m3<BLK, RPW, U>;
+  auto kern = k_gemv_e4m3<BLK, C>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)act_lds_bytes(kMaxInF));
+                                       (int)act_lds_bytes(C::MAX_IN_F));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int rows_per_wg = kWaves * RPW;
+  const int rows_per_wg = C::WAVES * C::RPW;
   const dim3 g((out_f + rows_per_wg - 1) / rows_per_wg, m);
-  hipLaunchKernelGGL(kern, g, dim3(kThreads), lds, s, W, row_bytes, scale, grid, grid_cols, qs,
-                     d, y, in_f, out_f);
+  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), act_lds_bytes(in_f), s, W, row_bytes, scale,
+                     grid, grid_cols, qs, d, y, in_f, out_f);
   return hipGetLastError();
+}
+
+// Shapes measured on MI355X: 4-wave workgroups with one row per wave and five windows in
+// flight up to in_f = 8192; 8 waves (so that the larger LDS row still allows 32 waves per CU)
+// up to 24576; 16 waves beyond.  All fit 64 VGPRs.
+using CfgSmall = Cfg<4, 1, 5, 2, 1>;   // in_f <= 8192
+using CfgMid = Cfg<8, 1, 5, 3, 2>;     // in_f <= 24576
+using CfgLarge = Cfg<16, 1, 5, 4, 4>;  // in_f <= 65536
+static_assert(CfgSmall::MAX_IN_F == 8192 && CfgMid::MAX_IN_F == 24576 &&
+                  CfgLarge::MAX_IN_F == kMaxInF, "activation coverage");
+static_assert(CfgSmall::KD * CfgSmall::THREADS * 32 >= CfgSmall::MAX_IN_F &&
+                  CfgMid::KD * CfgMid::THREADS * 32 >= CfgMid::MAX_IN_F &&
+                  CfgLarge::KD * CfgLarge::THREADS * 32 >= CfgLarge::MAX_IN_F,
+              "scale coverage");
+
+template <bool BLK>
+hipError_t dispatch(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
+                    int grid_cols, const int8_t *qs, const float *d, float *y, int m, int in_f,
+                    int out_f, hipStream_t s) {
+  if (in_f <= CfgSmall::MAX_IN_F)
+    return launch_cfg<BLK, CfgSmall>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+  if (in_f <= CfgMid::MAX_IN_F)
+    return launch_cfg<BLK, CfgMid>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+  return launch_cfg<BLK, CfgLarge>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
 }
 
 }  // namespace
@@ -187,9 +244,8 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
 hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                             int grid_cols, bool blk128, const int8_t *qs, const float *d,
                             float *y, int m, int in_f, int out_f, hipStream_t s) {
-  if (blk128)
-    return launch_cfg<true, 2, 4>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
-  return launch_cfg<false, 2, 4>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+  if (blk128) return dispatch<true>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+  return dispatch<false>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
 }
 
 }  // namespace fp8gemv

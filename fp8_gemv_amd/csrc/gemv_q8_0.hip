@@ -32,7 +32,7 @@
 namespace fp8gemv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // generic path
 constexpr int kWaves = kThreads / kWave;
 constexpr int kBlkBytes = 34;
 
@@ -41,11 +41,21 @@ __host__ __device__ constexpr int windows_per_row(int in_f) {
   return (chunks_per_row(in_f) + kWave - 1) / kWave;
 }
 
-// LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2],
-// then one scale table of nb + 2 floats per (wave, row).
-template <int RPW>
+// Launch shape of the fast path.  Each thread stages KQ activation blocks and KD block scales:
+// KQ * WAVES * 64 >= in_f / 32 and KD * WAVES * 64 >= in_f / 32 + 2.
+template <int WAVES_, int RPW_, int U_, int KQ_, int KD_>
+struct QCfg {
+  static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, KQ = KQ_, KD = KD_;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int MAX_IN_F = KQ * THREADS * 32;
+};
+
+// LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2], then
+// one scale table of nb + 2 floats per (wave, row).
+template <class C>
 __host__ __device__ constexpr size_t fast_lds_bytes(int in_f) {
-  return (size_t)windows_per_row(in_f) * 1024 + (size_t)(in_f / 32 + 2) * 4 * (1 + kWaves * RPW);
+  return (size_t)windows_per_row(in_f) * 1024 +
+         (size_t)(in_f / 32 + 2) * 4 * (1 + C::WAVES * C::RPW);
 }
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -53,22 +63,45 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int RPW, int U>
-__global__ __launch_bounds__(kThreads) void k_gemv_q8_0_fast(
-    const uint8_t *__restrict__ W, int64_t row_bytes, const int8_t *__restrict__ qs,
-    const float *__restrict__ d, float *__restrict__ y, int in_f, int out_f) {
+template <class C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
+                      const int8_t *__restrict__ qs, const float *__restrict__ d,
+                      float *__restrict__ y, int in_f, int out_f) {
+  constexpr int RPW = C::RPW, U = C::U, KQ = C::KQ, KD = C::KD, NTH = C::THREADS;
   extern __shared__ __align__(16) unsigned char lds[];
   const int nb = in_f / 32;
   const int cpr = chunks_per_row(in_f);
   const int nwin = windows_per_row(in_f);
-  uint8_t *shaped = lds;                                            // nwin * 1024 bytes
+  uint8_t *shaped = lds;                                              // nwin * 1024 bytes
   float *dsc = reinterpret_cast<float *>(lds + (size_t)nwin * 1024);  // nb + 2
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   float *stab = dsc + (nb + 2) * (1 + wave * RPW);  // RPW tables of nb + 2 floats
-  const int rbase = (blockIdx.x * kWaves + wave) * RPW;
+  const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
+  const int8_t *qa = qs + (int64_t)t * in_f;
+  const float *da = d + (int64_t)t * nb;
 
+  // 1. this thread's activation blocks and scales (oldest loads).
+  int4_t aq[KQ][2];
+  float dv[KD];
+#pragma unroll
+  for (int k = 0; k < KQ; ++k) {
+    const int b = threadIdx.x + k * NTH;
+    aq[k][0] = aq[k][1] = (int4_t){0, 0, 0, 0};
+    if (b < nb) {
+      aq[k][0] = *reinterpret_cast<const int4_t *>(qa + 32 * b);
+      aq[k][1] = *reinterpret_cast<const int4_t *>(qa + 32 * b + 16);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KD; ++k) {
+    const int b = threadIdx.x + k * NTH;
+    dv[k] = (b < nb) ? da[b] : 0.0f;
+  }
+
+  // 2. the first batch of weight loads.
   const uint8_t *wrow[RPW];
   bool rok[RPW];
 #pragma unroll
@@ -76,8 +109,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q8_0_fast(
     rok[r] = rbase + r < out_f;
     wrow[r] = W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + lane * 16;
   }
-
-  // First batch of weight loads, issued before the activation is staged.
   int4_t wv[U][RPW];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -88,29 +119,34 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q8_0_fast(
     }
   }
 
-  // Stage the activation in the shape of a Q8_0 row (zeros at the scale bytes and in the
-  // padding past the row), and the block scales d_a.
+  // 3. stage the activation in the shape of a Q8_0 row -- per block two zero bytes where the
+  // weight row has its fp16 scale, then the 32 qs -- with zeros past the row, and d_a.
   {
-    const int8_t *qa = qs + (int64_t)t * in_f;
     uint16_t *sh16 = reinterpret_cast<uint16_t *>(shaped);
-    for (int i = threadIdx.x; i < nwin * 512; i += kThreads) sh16[i] = 0;
-    __syncthreads();
-    for (int b = threadIdx.x; b < nb; b += kThreads) {
-      const int4_t q0 = *reinterpret_cast<const int4_t *>(qa + 32 * b);
-      const int4_t q1 = *reinterpret_cast<const int4_t *>(qa + 32 * b + 16);
-      uint16_t *dst = sh16 + (kBlkBytes * b + 2) / 2;  // 2-byte aligned
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dst[2 * j] = (uint16_t)(q0[j] & 0xFFFF);
-        dst[2 * j + 1] = (uint16_t)((uint32_t)q0[j] >> 16);
-        dst[8 + 2 * j] = (uint16_t)(q1[j] & 0xFFFF);
-        dst[8 + 2 * j + 1] = (uint16_t)((uint32_t)q1[j] >> 16);
+    for (int k = 0; k < KQ; ++k) {
+      const int b = threadIdx.x + k * NTH;
+      if (b < nb) {
+        uint16_t *dst = sh16 + (kBlkBytes / 2) * b;  // 2-byte aligned
+        dst[0] = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dst[1 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] & 0xFFFFu);
+            dst[2 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] >> 16);
+          }
+        }
       }
     }
-    const float *da = d + (int64_t)t * nb;
-    for (int b = threadIdx.x; b < nb + 2; b += kThreads) dsc[b] = (b < nb) ? da[b] : 0.0f;
-    __syncthreads();
+    for (int i = (kBlkBytes / 2) * nb + threadIdx.x; i < nwin * 512; i += NTH) sh16[i] = 0;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+      const int b = threadIdx.x + k * NTH;
+      if (b < nb + 2) dsc[b] = dv[k];
+    }
   }
+  __syncthreads();
 
   float acc[RPW];
 #pragma unroll
@@ -125,10 +161,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q8_0_fast(
       const bool live = c < cpr;
       // Chunk geometry (the same for every row): bytes [p0, p0 + 16) of the row.
       const int p0 = 16 * c;
-      const int b0 = p0 / kBlkBytes;              // block of the first byte
-      const int o = p0 - kBlkBytes * b0;          // offset inside that block, even, 0..32
-      const int hb = b0 + (o != 0);               // block whose scale may start in the chunk
-      const int hpos = kBlkBytes * hb - p0;       // its byte offset inside the chunk
+      const int b0 = p0 / kBlkBytes;         // block of the first byte
+      const int o = p0 - kBlkBytes * b0;     // offset inside that block, even, 0..32
+      const int hb = b0 + (o != 0);          // block whose scale may start in the chunk
+      const int hpos = kBlkBytes * hb - p0;  // its byte offset inside the chunk
       const bool has_scale = live && hpos <= 14;
       // dwords j < nlo hold quants of b0 (or its scale); the rest belong to b0 + 1.
       const int nlo = o <= 20 ? 4 : (o <= 24 ? 3 : (o <= 28 ? 2 : 1));
@@ -215,24 +251,35 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q8_0_generic(
   if (lane == 0) y[(int64_t)t * out_f + row] = s;
 }
 
-template <int RPW, int U>
+template <class C>
 hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, const float *d,
                        float *y, int m, int in_f, int out_f, hipStream_t s) {
-  auto kern = k_gemv_q8_0_fast<RPW, U>;
+  auto kern = k_gemv_q8_0_fast<C>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)fast_lds_bytes<RPW>(kMaxInF));
+                                       (int)fast_lds_bytes<C>(C::MAX_IN_F));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int rows_per_wg = kWaves * RPW;
+  const int rows_per_wg = C::WAVES * C::RPW;
   const dim3 g((out_f + rows_per_wg - 1) / rows_per_wg, m);
-  hipLaunchKernelGGL(kern, g, dim3(kThreads), fast_lds_bytes<RPW>(in_f), s, W, row_bytes, qs, d,
+  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes<C>(in_f), s, W, row_bytes, qs, d,
                      y, in_f, out_f);
   return hipGetLastError();
 }
+
+// Shapes as for the e4m3 stream: 4 waves up to in_f = 8192, 8 up to 24576, 16 beyond; a row
+// of in_f = 5120 is 6 windows (the last one partly used), so U = 6 covers it in one batch.
+using QSmall = QCfg<4, 1, 6, 1, 2>;   // in_f <= 8192
+using QMid = QCfg<8, 1, 6, 2, 3>;     // in_f <= 32768
+using QLarge = QCfg<16, 1, 6, 2, 3>;  // in_f <= 65536
+static_assert(QLarge::MAX_IN_F == kMaxInF, "activation coverage");
+static_assert(QSmall::KD * QSmall::THREADS >= QSmall::MAX_IN_F / 32 + 2 &&
+                  QMid::KD * QMid::THREADS >= QMid::MAX_IN_F / 32 + 2 &&
+                  QLarge::KD * QLarge::THREADS >= QLarge::MAX_IN_F / 32 + 2,
+              "scale coverage");
 
 }  // namespace
 
@@ -240,7 +287,11 @@ hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *q
                             const float *d, float *y, int m, int in_f, int out_f, hipStream_t s) {
   const bool fast = (in_f % 256 == 0) && (row_bytes % 16 == 0) &&
                     ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
-  if (fast) return launch_fast<2, 4>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+  if (fast) {
+    if (in_f <= 8192) return launch_fast<QSmall>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+    if (in_f <= 24576) return launch_fast<QMid>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+    return launch_fast<QLarge>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+  }
   const dim3 g((out_f + kWaves - 1) / kWaves, m);
   hipLaunchKernelGGL(k_gemv_q8_0_generic, g, dim3(kThreads), 0, s, W, row_bytes, qs, d, y, in_f,
                      out_f);

@@ -212,3 +212,44 @@ def test_one_hip_runtime_in_process(fg):
     maps = open(f"/proc/{os.getpid()}/maps").read().splitlines()
     libs = {line.split()[-1] for line in maps if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+def test_graph_replays_match_eager(fg):
+    # The bench replays the hot path from a HIP graph: every replay, with eager work and
+    # synchronisations between replays, must reproduce the eager bytes.
+    case("graph replay of producer + three GEMVs")
+    in_f, out_f = 2048, 768
+    x = to_dev(synth.x_rows(in_f, 1))
+    w = to_dev(synth.gain(in_f))
+    qs = torch.empty((1, in_f), dtype=torch.int8, device=dev())
+    d = torch.empty((1, in_f // 32), device=dev())
+    cases = [Case(k, out_f, in_f, 1) for k in KINDS]
+    ys = [torch.empty((1, out_f), device=dev()) for _ in KINDS]
+
+    def run():
+        fg.rmsnorm_q8_1(x, w, None, qs, d, in_f, 1)
+        for c, y in zip(cases, ys):
+            if c.kind == "q8_0":
+                fg.gemv_q8_0_q81(c.Wd, c.row_bytes, qs, d, y, 1, in_f, out_f)
+            elif c.kind == "e4m3":
+                fg.gemv_e4m3_q81(c.Wd, c.row_bytes, SCALE, qs, d, y, 1, in_f, out_f)
+            else:
+                fg.gemv_e4m3_blk128_q81(c.Wd, c.row_bytes, c.gd, c.grid.shape[1], qs, d, y, 1,
+                                        in_f, out_f)
+
+    run()
+    eager = [host(y).copy() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        qs.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = [host(y) for y in ys]
+        for e, gy in zip(eager, got):
+            assert e.tobytes() == gy.tobytes(), rep
+        run()  # eager work between replays
+        torch.cuda.synchronize()
