@@ -2,9 +2,10 @@
 """Bench: the m=1 decode matvec hot path on one MI355X, DRAM-cold.
 
 One step = for each 27B-class projection shape [out_f, in_f] in {5120x5120, 17408x5120,
-5120x17408} and for each weight container (per-tensor e4m3, block-128 e4m3, Q8_0), in that
-interleaved order: the fused producer rmsnorm_q8_1 on the f32 activation row, then the GEMV on
-the next rotated copy of that container's weights -- 9 producer + 9 GEMV launches.
+5120x17408}: the fused producer rmsnorm_q8_1 on the f32 activation row, then -- interleaved --
+the GEMV of each weight container (per-tensor e4m3, block-128 e4m3, Q8_0) on the next rotated
+copy of that container's weights, all three consuming the same q8_1 row: 3 producer + 9 GEMV
+launches.
 (gemv_e4m3_bench.rs: the three arms interleaved per iteration, each on its own weight copies,
 each block-128 grid rotating with its copy; q8_fuse_gate.rs: the fused producer.)
 
@@ -119,9 +120,12 @@ def cpu_baseline(shapes, arms, threads: int):
 
     t0 = time.perf_counter()
     wbytes = 0
+    acts = {}
     for arm, out_f, in_f, x, w, W, g in work:
-        ref = oracle.rmsnorm_q8_1(x, w)
-        qs, d = ref["qs"], ref["d"]
+        if (out_f, in_f) not in acts:
+            ref = oracle.rmsnorm_q8_1(x, w)
+            acts[(out_f, in_f)] = (ref["qs"], ref["d"])
+        qs, d = acts[(out_f, in_f)]
         step = (out_f + threads - 1) // threads
         futs = [pool.submit(gemv, arm, out_f, in_f, W, g, qs, d, (r, min(out_f, r + step)))
                 for r in range(0, out_f, step)]
@@ -132,7 +136,7 @@ def cpu_baseline(shapes, arms, threads: int):
     pool.shutdown()
     return {"value": round(wbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "ms_per_step": round(secs * 1e3, 1),
-            "sample": "one full step: rmsnorm_q8_1 + the 9 GEMVs (3 shapes x 3 containers), "
+            "sample": "one full step: rmsnorm_q8_1 per shape + the 9 GEMVs (3 shapes x 3 containers), "
                       "f64 oracle, output rows split over host threads"}
 
 
@@ -189,8 +193,8 @@ def main() -> int:
 
     def step():
         for out_f, in_f in shapes:
+            qs, d = producer((out_f, in_f))
             for a in arms:
-                qs, d = producer((out_f, in_f))
                 arm_objs[(out_f, in_f, a)].launch(qs, d)
 
     def timed(fn, n_inner):
@@ -290,9 +294,10 @@ def main() -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3/int8 x int8 -> f32", "data": "synthetic",
-        "config": {"workload": "m=1 decode matvec step: rmsnorm_q8_1 + GEMV for e4m3, "
-                               "e4m3-blk128 and Q8_0 weights at [out_f,in_f] 5120x5120, "
-                               "17408x5120, 5120x17408, interleaved, DRAM-cold rotation",
+        "config": {"workload": "m=1 decode matvec step: per shape rmsnorm_q8_1 then GEMVs of "
+                               "e4m3, e4m3-blk128 and Q8_0 weights on that q8_1 row, "
+                               "[out_f,in_f] 5120x5120, 17408x5120, 5120x17408, interleaved, "
+                               "DRAM-cold rotation",
                    "m": 1, "shapes": [f"{o}x{i}" for o, i in shapes], "arms": arms,
                    "eps": EPS, "e4m3_scale": SCALE},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -28,7 +28,7 @@ int rms_norm_f32(const float *x, const float *w, float *z, int ncols, int nrows,
                  void *stream) {
   if (!x || !w || !z) return FP8GEMV_ERR_NULL;
   if (nrows < 1 || bad_cols(ncols)) return FP8GEMV_ERR_SHAPE;
-  if (ncols > FP8GEMV_MAX_IN_F) return FP8GEMV_ERR_TOO_LARGE;
+  if (ncols > FP8GEMV_MAX_IN_F || nrows > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(z, 16)) return FP8GEMV_ERR_ALIGN;
   return launch_rc(fp8gemv::launch_rms_norm(x, w, z, ncols, nrows, eps, (hipStream_t)stream));
 }
@@ -45,7 +45,7 @@ int rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d,
                  int nrows, float eps, void *stream) {
   if (!x || !w || !qs || !d) return FP8GEMV_ERR_NULL;
   if (nrows < 1 || bad_cols(ncols)) return FP8GEMV_ERR_SHAPE;
-  if (ncols > FP8GEMV_MAX_IN_F) return FP8GEMV_ERR_TOO_LARGE;
+  if (ncols > FP8GEMV_MAX_IN_F || nrows > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
   if (!aligned(x, 16) || !aligned(w, 16) || (z && !aligned(z, 16)) || !aligned(qs, 16) ||
       !aligned(d, 4))
     return FP8GEMV_ERR_ALIGN;

@@ -23,7 +23,9 @@
 //     scaled separately.
 //   * A chunk contains at most one block scale.  The lane holding it converts it
 //     (fp16 -> f32, times the activation scale d_a[b]) and publishes it in a per-wave LDS
-//     table; the lanes that need it read it back after a wave-local fence.
+//     ring of 64 entries indexed by block mod 64 (the blocks live at any one time span at
+//     most 33 consecutive indices); the lanes that need it read it back after a wave-local
+//     fence.
 // Generic path (any in_f % 32 == 0): one lane per block, 2-byte loads; correct, not tuned.
 // Row t = blockIdx.y of the activation runs identical code, so each activation row of an
 // m-row call is bit-identical to an m=1 call on that row.
@@ -50,12 +52,14 @@ struct QCfg {
   static constexpr int MAX_IN_F = KQ * THREADS * 32;
 };
 
+constexpr int kRing = 64;  // scale-ring entries per (wave, row)
+
 // LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2], then
-// one scale table of nb + 2 floats per (wave, row).
+// one scale ring of kRing floats per (wave, row).
 template <class C>
 __host__ __device__ constexpr size_t fast_lds_bytes(int in_f) {
-  return (size_t)windows_per_row(in_f) * 1024 +
-         (size_t)(in_f / 32 + 2) * 4 * (1 + C::WAVES * C::RPW);
+  return (size_t)windows_per_row(in_f) * 1024 + (size_t)(in_f / 32 + 2) * 4 +
+         (size_t)C::WAVES * C::RPW * kRing * 4;
 }
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -78,7 +82,7 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  float *stab = dsc + (nb + 2) * (1 + wave * RPW);  // RPW tables of nb + 2 floats
+  float *stab = dsc + (nb + 2) + wave * RPW * kRing;  // RPW rings of kRing floats
   const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
   const int8_t *qa = qs + (int64_t)t * in_f;
   const float *da = d + (int64_t)t * nb;
@@ -179,7 +183,7 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
           const int q = hpos >> 2;
           const uint32_t dw = q == 0 ? w[0] : (q == 1 ? w[1] : (q == 2 ? w[2] : w[3]));
           const uint16_t hbits = (hpos & 2) ? (uint16_t)(dw >> 16) : (uint16_t)(dw & 0xFFFF);
-          stab[r * (nb + 2) + hb] = (float)__builtin_bit_cast(_Float16, hbits) * da_h;
+          stab[r * kRing + (hb % kRing)] = (float)__builtin_bit_cast(_Float16, hbits) * da_h;
         }
       }
       wave_lds_fence();
@@ -192,9 +196,9 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
         const int t4 = __builtin_amdgcn_sdot4(w[3], a[3], t3, false);
         const int s_lo = nlo == 4 ? t4 : (nlo == 3 ? t3 : (nlo == 2 ? t2 : t1));
         const int s_hi = t4 - s_lo;
-        const float *tab = stab + r * (nb + 2);
-        const float S0 = live ? tab[b0] : 0.0f;
-        const float S1 = (live && nlo < 4) ? tab[b0 + 1] : 0.0f;
+        const float *tab = stab + r * kRing;
+        const float S0 = live ? tab[b0 % kRing] : 0.0f;
+        const float S1 = (live && nlo < 4) ? tab[(b0 + 1) % kRing] : 0.0f;
         acc[r] = fmaf((float)s_lo, S0, acc[r]);
         acc[r] = fmaf((float)s_hi, S1, acc[r]);
       }

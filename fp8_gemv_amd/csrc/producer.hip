@@ -8,6 +8,11 @@
 // for a 32-block) with the same workgroup shape, and quantisation of a block depends only on
 // that block's 32 values.
 //
+// Parallel shape: one workgroup per (1024-column slice, row).  Every workgroup of a row
+// computes the row's RMS factor itself from the whole row (same function, same order, so the
+// same bits everywhere) and then normalises and quantises only its slice: no inter-workgroup
+// communication, and a single row is spread over ceil(ncols / 1024) CUs.
+//
 // Numerics (this file is compiled with -ffp-contract=off):
 //   ss  = sum_j x_j^2, every square exact in f64, accumulated as a double-double and rounded
 //         once to f64, so ss is the correctly rounded sum except in vanishingly rare ties;
@@ -40,16 +45,25 @@ __device__ __forceinline__ void dd_add(double &hi, double &lo, double ohi, doubl
 // returns the same value.  `red` is LDS scratch for 2 doubles per wave.
 __device__ double row_scale(const float *__restrict__ x, int ncols, float eps, double *red) {
   double hi = 0.0, lo = 0.0;
-  for (int j = threadIdx.x * 4; j < ncols; j += kColsPerPass) {
-    const float4 v = *reinterpret_cast<const float4 *>(x + j);
-    const float e4[4] = {v.x, v.y, v.z, v.w};
+  constexpr int kBatch = 8;  // loads issued together before they are accumulated
+  for (int base = threadIdx.x * 4; base < ncols; base += kBatch * kColsPerPass) {
+    float4 v[kBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double p = (double)e4[i] * (double)e4[i];
-      double s, e;
-      two_sum(hi, p, s, e);
-      hi = s;
-      lo += e;
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = base + u * kColsPerPass;
+      v[u] = j < ncols ? *reinterpret_cast<const float4 *>(x + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double p = (double)e4[i] * (double)e4[i];
+        double s, e;
+        two_sum(hi, p, s, e);
+        hi = s;
+        lo += e;
+      }
     }
   }
   // Butterfly over the wave: both partners of a pair compute the same (commutative) result.
@@ -101,10 +115,11 @@ __global__ __launch_bounds__(kThreads) void k_rms_norm(const float *__restrict__
                                                        float *__restrict__ z, int ncols,
                                                        float eps) {
   __shared__ double red[2 * kThreads / kWave];
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.y;
   const float *xr = x + row * ncols;
   const double s = row_scale(xr, ncols, eps, red);
-  for (int j = threadIdx.x * 4; j < ncols; j += kColsPerPass) {
+  const int j = blockIdx.x * kColsPerPass + threadIdx.x * 4;
+  if (j < ncols) {
     const float4 xv = *reinterpret_cast<const float4 *>(xr + j);
     const float4 wv = *reinterpret_cast<const float4 *>(w + j);
     float4 zv;
@@ -143,29 +158,27 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm_q8_1(const float *__restri
                                                            float *__restrict__ d, int ncols,
                                                            float eps) {
   __shared__ double red[2 * kThreads / kWave];
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.y;
   const float *xr = x + row * ncols;
   const double s = row_scale(xr, ncols, eps, red);
-  for (int base = 0; base < ncols; base += kColsPerPass) {
-    const int j = base + threadIdx.x * 4;
-    const bool live = j < ncols;
-    float zv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
-      const float4 xv = *reinterpret_cast<const float4 *>(xr + j);
-      const float4 wv = *reinterpret_cast<const float4 *>(w + j);
-      zv[0] = z_value(xv.x, wv.x, s);
-      zv[1] = z_value(xv.y, wv.y, s);
-      zv[2] = z_value(xv.z, wv.z, s);
-      zv[3] = z_value(xv.w, wv.w, s);
-      if (z != nullptr)
-        *reinterpret_cast<float4 *>(z + row * ncols + j) = make_float4(zv[0], zv[1], zv[2], zv[3]);
-    }
-    float db;
-    const uint32_t packed = quant_group(zv, db);
-    if (live) {
-      *reinterpret_cast<uint32_t *>(qs + row * ncols + j) = packed;
-      if ((threadIdx.x & 7) == 0) d[row * (ncols / 32) + j / 32] = db;
-    }
+  const int j = blockIdx.x * kColsPerPass + threadIdx.x * 4;
+  const bool live = j < ncols;  // whole 8-lane groups are live or not (ncols % 32 == 0)
+  float zv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const float4 xv = *reinterpret_cast<const float4 *>(xr + j);
+    const float4 wv = *reinterpret_cast<const float4 *>(w + j);
+    zv[0] = z_value(xv.x, wv.x, s);
+    zv[1] = z_value(xv.y, wv.y, s);
+    zv[2] = z_value(xv.z, wv.z, s);
+    zv[3] = z_value(xv.w, wv.w, s);
+    if (z != nullptr)
+      *reinterpret_cast<float4 *>(z + row * ncols + j) = make_float4(zv[0], zv[1], zv[2], zv[3]);
+  }
+  float db;
+  const uint32_t packed = quant_group(zv, db);
+  if (live) {
+    *reinterpret_cast<uint32_t *>(qs + row * ncols + j) = packed;
+    if ((threadIdx.x & 7) == 0) d[row * (ncols / 32) + j / 32] = db;
   }
 }
 
@@ -173,7 +186,8 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm_q8_1(const float *__restri
 
 hipError_t launch_rms_norm(const float *x, const float *w, float *z, int ncols, int nrows,
                            float eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_rms_norm, dim3(nrows), dim3(kThreads), 0, s, x, w, z, ncols, eps);
+  const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
+  hipLaunchKernelGGL(k_rms_norm, grid, dim3(kThreads), 0, s, x, w, z, ncols, eps);
   return hipGetLastError();
 }
 
@@ -186,8 +200,8 @@ hipError_t launch_quantize_q8_1(const float *z, int8_t *qs, float *d, int nrows,
 
 hipError_t launch_rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d,
                                int ncols, int nrows, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm_q8_1, dim3(nrows), dim3(kThreads), 0, s, x, w, z, qs, d, ncols,
-                     eps);
+  const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
+  hipLaunchKernelGGL(k_rmsnorm_q8_1, grid, dim3(kThreads), 0, s, x, w, z, qs, d, ncols, eps);
   return hipGetLastError();
 }
 

@@ -43,8 +43,9 @@ extern "C" {
 #define FP8GEMV_ERR_ALIGN      (-5) /* a pointer or row stride breaks the stated alignment */
 #define FP8GEMV_ERR_TOO_LARGE  (-6) /* a size beyond the stated limit */
 
-/* Limits.  in_f is bounded so that one activation row (staged in LDS) fits a workgroup;
- * m is bounded by the launch grid's y dimension used for activation rows. */
+/* Limits.  in_f (and the producer's ncols) is bounded so that one activation row staged in
+ * LDS fits a workgroup; m (and the producer's nrows) is bounded by the launch grid's y
+ * dimension, which indexes rows. */
 #define FP8GEMV_MAX_IN_F   65536
 #define FP8GEMV_MAX_M      65535
 
@@ -55,7 +56,8 @@ extern "C" {
  *   x    f32 [nrows, ncols]   input rows
  *   w    f32 [ncols]          gain, broadcast over rows
  *   z    f32 [nrows, ncols]   output (may not alias x or w)
- *   ncols multiple of 32, <= FP8GEMV_MAX_IN_F; nrows >= 1; eps as given (1e-6 on the page)
+ *   ncols multiple of 32, <= FP8GEMV_MAX_IN_F; 1 <= nrows <= FP8GEMV_MAX_M; eps as given
+ *   (1e-6 on the page)
  * Arithmetic: the sum of squares is accumulated in double-double and rounded once to f64,
  * s = 1 / sqrt(ss / ncols + eps) in f64, z = (float)((double)x * w * s).
  * Alignment: x, w, z 16-byte aligned.
@@ -73,7 +75,8 @@ int rms_norm_f32(const float *x, const float *w, float *z, int ncols, int nrows,
  *   z   f32 [nrows, ncols]      input
  *   qs  int8 [nrows, ncols]     output
  *   d   f32 [nrows, ncols / 32] output
- * Argument order follows the page (nrows before ncols).  Alignment: z, qs, d 16-byte aligned.
+ * Argument order follows the page (nrows before ncols).  Limits as for rms_norm_f32.
+ * Alignment: z and qs 16-byte aligned, d 4-byte aligned.
  */
 int quantize_q8_1(const float *z, int8_t *qs, float *d, int nrows, int ncols, void *stream);
 
