@@ -140,6 +140,126 @@ def cpu_baseline(shapes, arms, threads: int):
                       "f64 oracle, output rows split over host threads"}
 
 
+# ------------------------------------------------------------------ profile summaries
+PROFILES = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILES, "gemv_hbm_counters.md")
+GEMV_SOURCES = ["fp8_gemv_amd/csrc/common.hpp", "fp8_gemv_amd/csrc/gemv_e4m3.hip",
+                "fp8_gemv_amd/csrc/gemv_q8_0.hip"]
+CALIB_MIB = 512
+
+
+def gemv_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMV_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    return name.replace("void ", "").replace("fp8gemv::(anonymous namespace)::", "").split("(")[0]
+
+
+def _kernel_key(name: str, grid: str, wg: str) -> str:
+    return f"{_short(name)} grid={grid} wg={wg}"
+
+
+def launch_signature(arm: str, out_f: int, in_f: int):
+    """(kernel family, grid threads, workgroup size, LDS bytes) of the library's launch for
+    one GEMV -- the launch-shape choice of the HIP library restated for labelling profiles."""
+    waves = 4 if in_f <= 8192 else (8 if in_f <= 24576 else 16)
+    wg = waves * 64
+    grid = -(-out_f // waves) * wg
+    if arm == "q8_0":
+        nb = in_f // 32
+        nwin = -(-(nb * 34 // 16) // 64)
+        lds = nwin * 1024 + (nb + 2) * 4 + waves * 64 * 4 + 48
+        return ("k_gemv_q8_0_fast", grid, wg, lds)
+    lds = -(-in_f // 1024) * 2176 + 32
+    return ("k_gemv_e4m3<true" if arm == "blk128" else "k_gemv_e4m3<false", grid, wg, lds)
+
+
+def _label_of(name: str, grid: int, wg: int, lds: int) -> str:
+    for out_f, in_f in SHAPES:
+        for arm in ARMS:
+            fam, g, w, _ = launch_signature(arm, out_f, in_f)
+            # rocprofv3 reports only static LDS, so (family, grid, workgroup) is the key; it is
+            # unique over the bench's nine launches.
+            if _short(name).startswith(fam) and (g, w) == (grid, wg):
+                return f"{arm}@{out_f}x{in_f}"
+    return "-"
+
+
+def summarize_trace(csv_path: str) -> str:
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(csv_path)))
+    by = {}
+    for r in rows:
+        k = _kernel_key(r["Kernel_Name"], r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"],
+                        r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"])
+        by.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = ["| kernel (grid = threads) | calls | avg us | median us | min us | max us |",
+           "|---|---|---|---|---|---|"]
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {k} | {len(v)} | {statistics.mean(v) / 1e3:.3f} | "
+                   f"{statistics.median(v) / 1e3:.3f} | {min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} |")
+    return "\n".join(out)
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
+    """Median FETCH_SIZE / WRITE_SIZE (KiB) per GEMV launch shape, with the scale factors that
+    make the same counters read the known size of the calibration copy."""
+    import csv
+    import statistics
+
+    def load(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], r["Grid_Size"], r["Workgroup_Size"],
+                                              r["LDS_Block_Size"], float(r["Counter_Value"]))
+        return out
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    known_kib = CALIB_MIB * 1024
+    calib = [i for i, v in write.items() if "copyBuffer" in v[0] and abs(v[4] - known_kib) < 1]
+    fscale = known_kib / statistics.median(fetch[i][4] for i in calib)
+    wscale = known_kib / statistics.median(write[i][4] for i in calib)
+    by = {}
+    for i, (name, grid, wg, lds, fv) in fetch.items():
+        if "gemv" not in name or i not in write:
+            continue
+        key = (f"label={_label_of(name, int(grid), int(wg), int(lds))} ",
+               _kernel_key(name, grid, wg))
+        by.setdefault(key, []).append((fv, write[i][4]))
+    lines = [f"fetch_scale {fscale:.4f}", f"write_scale {wscale:.4f}",
+             f"calibration: {len(calib)} device copies of {CALIB_MIB} MiB",
+             "", "| launch | kernel (grid = threads) | launches | FETCH_SIZE KiB | "
+                 "WRITE_SIZE KiB | HBM bytes |", "|---|---|---|---|---|---|"]
+    for (label, k), v in sorted(by.items()):
+        f = statistics.median(x[0] for x in v)
+        w = statistics.median(x[1] for x in v)
+        lines.append(f"| {label}| {k} | {len(v)} | {f:.1f} | {w:.1f} | "
+                     f"{round((f * fscale + w * wscale) * 1024)} |")
+    return "\n".join(lines)
+
+
+def traffic_for(kernel_label: str):
+    """HBM bytes per launch of a GEMV from the committed counter summary, or None when the
+    summary is missing, does not cover this launch, or was taken on other kernel sources."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    if f"source {gemv_source_hash()}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("| ") and f"label={kernel_label} " in line:
+            return int(line.rstrip(" |").split("|")[-1])
+    return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,7 +272,24 @@ def main() -> int:
     ap.add_argument("--shapes", default="all", help="comma list like 17408x5120 (out x in)")
     ap.add_argument("--arms", default=",".join(ARMS))
     ap.add_argument("--jsonl", default="", help="append per-(shape, container) rows here")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="time only the per-kernel GEMV loops (short runs under a profiler)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run 4 device-to-device copies of this many MiB (a plain copy "
+                         "kernel of known size that calibrates the HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print a markdown summary of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM byte-counter summary of two rocprofv3 --pmc runs, exit")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_pmc:
+        print(f"source {gemv_source_hash()}")
+        print(summarize_pmc(*args.summarize_pmc))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -215,24 +352,39 @@ def main() -> int:
         torch.cuda.synchronize()
         return g
 
+    if args.copy_mib:
+        nbytes = args.copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copies: 4 x {args.copy_mib} MiB")
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} eager steps done")
 
-    # Eager steps: one host launch per kernel (bound by host launch rate, kept for reference).
-    t0 = time.perf_counter()
-    eager_ms = timed(lambda: [step() for _ in range(args.steps)], args.steps)
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # The timed region: K steps captured once as a HIP graph, replayed after one untimed replay.
-    graph = capture(lambda: [step() for _ in range(args.steps)])
-    graph.replay()
-    torch.cuda.synchronize()
-    ms_per_step = timed(graph.replay, args.steps)
     step_wbytes = sum(weight_bytes(a, o, i) for (o, i, a) in arm_objs)
-    value = step_wbytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step:.4f} ms (graph), eager {eager_ms:.4f} ms, {value:.1f} GB/s of weights")
+    eager_ms = wall_ms = ms_per_step = value = float("nan")
+    if not args.kernels_only:
+        # Eager steps: one host launch per kernel (bound by host launch rate; reference only).
+        t0 = time.perf_counter()
+        eager_ms = timed(lambda: [step() for _ in range(args.steps)], args.steps)
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+        # The timed region: K steps captured once as a HIP graph, replayed after one untimed
+        # replay.
+        graph = capture(lambda: [step() for _ in range(args.steps)])
+        graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = timed(graph.replay, args.steps)
+        value = step_wbytes / (ms_per_step * 1e-3) / 1e9
+        log(f"step {ms_per_step:.4f} ms (graph), eager {eager_ms:.4f} ms, "
+            f"{value:.1f} GB/s of weights")
 
     # Per-kernel timing: one GEMV launched back to back over its rotated copies, captured as a
     # graph and bracketed by HIP events on the launch stream; q8_1 produced once before.
@@ -256,7 +408,7 @@ def main() -> int:
 
     # Producer alone (latency-bound; the gate page's site widths), fused vs two-launch chain.
     prod_us = {}
-    for ncols in (1536, 4096, 8192):
+    for ncols in (() if args.kernels_only else (1536, 4096, 8192)):
         x = torch.from_numpy(synth.x_rows(ncols, 1)).to(dev)
         w = torch.from_numpy(synth.gain(ncols)).to(dev)
         z = torch.empty(ncols, device=dev)
@@ -279,8 +431,9 @@ def main() -> int:
     dom = detail[dom_key]
     achieved = dom["alg_bytes"] / (dom["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": dom_key}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for(dom_key), "kernel": dom_key,
+                "alg_bytes": dom["alg_bytes"], "us": dom["us"]}
 
     cpu = None
     if not args.no_cpu:

@@ -45,9 +45,32 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ----------------------------------------------------------------------- loads ----
+// Raw buffer resource over [base, base + bytes).  Loads through it at offsets past `bytes`
+// return zeros and touch no memory, so every load can be issued unconditionally: no
+// branches around loads means the compiler can count outstanding loads exactly and wait
+// only for the one it needs.  `base` must be wave-uniform.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, no swizzle
+constexpr int kAuxNonTemporal = 2;      // "nt": streamed once, do not keep
+
+__device__ __forceinline__ rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
 // 16-byte streaming load of weight bytes: read once, never reused, so marked non-temporal.
-__device__ __forceinline__ int4_t load_stream16(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const int4_t *>(p));
+__device__ __forceinline__ int4_t buf_load16_stream(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0,
+                                                                          kAuxNonTemporal));
+}
+__device__ __forceinline__ int4_t buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+// The wave index as a value the compiler knows to be uniform.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
 }
 
 }  // namespace fp8gemv

@@ -44,6 +44,10 @@ __host__ __device__ constexpr int num_windows(int in_f) { return (in_f + kWinCol
 __host__ __device__ constexpr size_t act_lds_bytes(int in_f) {
   return (size_t)num_windows(in_f) * (kWinCols * 2 + (kWinCols / 32) * 4);
 }
+// Plus a 32-byte sink that takes the staging writes of threads with nothing to stage, so
+// that the staging code has no branches (a branch would let the compiler sink an activation
+// load behind the weight loads and then wait for all of them).
+constexpr size_t kSinkBytes = 32;
 
 // int8 x4 -> two f16 pairs, exactly: after flipping the sign bit a byte u is 0..255 and the
 // f16 with bits 0x6400 | u is 1024 + u; subtracting 1152 leaves the signed value.
@@ -91,67 +95,65 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
 
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = wave_id();
   const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
-  const int8_t *qa = qs + (int64_t)t * in_f;
-  const float *da = d + (int64_t)t * (in_f / 32);
+  const int nb = in_f / 32;
+  const rsrc_t qrs = buf_rsrc(qs + (int64_t)t * in_f, (uint32_t)in_f);
+  const rsrc_t drs = buf_rsrc(d + (int64_t)t * nb, (uint32_t)nb * 4);
 
-  // 1. this thread's share of the activation row (oldest loads).
+  // 1. this thread's share of the activation row (oldest loads; zeros past in_f).
   int4_t aq[K];
   float dv[KD];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int c = (threadIdx.x + k * NTH) * 16;
-    aq[k] = (int4_t){0, 0, 0, 0};
-    if (c < in_f) aq[k] = *reinterpret_cast<const int4_t *>(qa + c);
-  }
-  // Grid row of this workgroup (its rows all lie in one 128-row tile); clamped so a
-  // workgroup past the last row still reads inside the grid.
-  const int rfirst = blockIdx.x * C::WAVES * RPW;
-  const float *grow =
-      BLK ? grid + (int64_t)((rfirst < out_f ? rfirst : out_f - 1) / 128) * grid_cols : nullptr;
+  for (int k = 0; k < K; ++k) aq[k] = buf_load16(qrs, (uint32_t)(threadIdx.x + k * NTH) * 16);
 #pragma unroll
-  for (int k = 0; k < KD; ++k) {
-    const int b = threadIdx.x + k * NTH;
-    dv[k] = 0.0f;
-    if (b < in_f / 32) dv[k] = BLK ? da[b] * grow[b / 4] : da[b];
+  for (int k = 0; k < KD; ++k) dv[k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
+  if (BLK) {
+    // Grid row of this workgroup (its rows all lie in one 128-row tile); clamped so a
+    // workgroup past the last row still reads inside the grid.
+    const int rfirst = blockIdx.x * C::WAVES * RPW;
+    const int grow = (rfirst < out_f ? rfirst : out_f - 1) / 128;
+    const rsrc_t grs = buf_rsrc(grid + (int64_t)grow * grid_cols, (uint32_t)grid_cols * 4);
+#pragma unroll
+    for (int k = 0; k < KD; ++k) dv[k] *= buf_load_f32(grs, (uint32_t)((threadIdx.x + k * NTH) / 4) * 4);
   }
 
-  // 2. the first batch of weight loads.
-  const uint8_t *wrow[RPW];
+  // 2. the first batch of weight loads: one resource per row over its first in_f bytes (no
+  // bytes for a row past out_f), so out-of-range windows and rows read as zeros.
+  rsrc_t wrs[RPW];
   bool rok[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     rok[r] = rbase + r < out_f;
-    wrow[r] = W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + lane * 16;
+    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes,
+                      rok[r] ? (uint32_t)in_f : 0u);
   }
   int4_t wv[U][RPW];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int col = u * kWinCols + lane * 16;
-      wv[u][r] = (int4_t){0, 0, 0, 0};
-      if (rok[r] && col < in_f) wv[u][r] = load_stream16(wrow[r] + u * kWinCols);
-    }
+    for (int r = 0; r < RPW; ++r)
+      wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)(u * kWinCols + lane * 16));
   }
 
-  // 3. stage the activation (f16) and its scales in LDS; zero past in_f.
+  // 3. stage the activation (f16) and its scales in LDS; zeros past in_f.  Threads past the
+  // staged range write into the sink instead of branching around the store.
+  unsigned char *sink = lds + act_lds_bytes(in_f);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int c = (threadIdx.x + k * NTH) * 16;
-    if (c < nwin * kWinCols) {
-      half2_t h[8];
+    half2_t h[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) i8x4_to_f16((uint32_t)aq[k][j], h[2 * j], h[2 * j + 1]);
-      *reinterpret_cast<int4_t *>(act + c) = *reinterpret_cast<const int4_t *>(h);
-      *reinterpret_cast<int4_t *>(act + c + 8) = *reinterpret_cast<const int4_t *>(h + 4);
-    }
+    for (int j = 0; j < 4; ++j) i8x4_to_f16((uint32_t)aq[k][j], h[2 * j], h[2 * j + 1]);
+    _Float16 *dst = c < nwin * kWinCols ? act + c : reinterpret_cast<_Float16 *>(sink);
+    *reinterpret_cast<int4_t *>(dst) = *reinterpret_cast<const int4_t *>(h);
+    *reinterpret_cast<int4_t *>(dst + 8) = *reinterpret_cast<const int4_t *>(h + 4);
   }
 #pragma unroll
   for (int k = 0; k < KD; ++k) {
     const int b = threadIdx.x + k * NTH;
-    if (b < nwin * (kWinCols / 32)) dsc[b] = dv[k];
+    float *dst = b < nwin * (kWinCols / 32) ? dsc + b : reinterpret_cast<float *>(sink);
+    *dst = dv[k];
   }
   __syncthreads();
 
@@ -173,18 +175,13 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
         for (int r = 0; r < RPW; ++r) acc[r] = fmaf(dot16(wv[u][r], a), sc, acc[r]);
       }
     }
+    // Next batch, issued unconditionally (past the row it reads zeros and no memory).
     const int nxt = w0 + U;
-    if (nxt < nwin) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const int col = (nxt + u) * kWinCols + lane * 16;
-          wv[u][r] = (int4_t){0, 0, 0, 0};
-          if (rok[r] && col < in_f)
-            wv[u][r] = load_stream16(wrow[r] + (int64_t)(nxt + u) * kWinCols);
-        }
-      }
+      for (int r = 0; r < RPW; ++r)
+        wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)((nxt + u) * kWinCols + lane * 16));
     }
   }
 
@@ -204,13 +201,13 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)act_lds_bytes(C::MAX_IN_F));
+                                       (int)(act_lds_bytes(C::MAX_IN_F) + kSinkBytes));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int rows_per_wg = C::WAVES * C::RPW;
   const dim3 g((out_f + rows_per_wg - 1) / rows_per_wg, m);
-  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), act_lds_bytes(in_f), s, W, row_bytes, scale,
+  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), act_lds_bytes(in_f) + kSinkBytes, s, W, row_bytes, scale,
                      grid, grid_cols, qs, d, y, in_f, out_f);
   return hipGetLastError();
 }

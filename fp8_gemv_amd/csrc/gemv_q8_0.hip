@@ -56,10 +56,14 @@ constexpr int kRing = 64;  // scale-ring entries per (wave, row)
 
 // LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2], then
 // one scale ring of kRing floats per (wave, row).
+// Last: a 48-byte sink that takes the staging writes of threads with nothing to stage, so
+// that the staging code has no branches (a branch would let the compiler sink an activation
+// load behind the weight loads and then wait for all of them).
+constexpr size_t kSinkBytes = 48;
 template <class C>
 __host__ __device__ constexpr size_t fast_lds_bytes(int in_f) {
   return (size_t)windows_per_row(in_f) * 1024 + (size_t)(in_f / 32 + 2) * 4 +
-         (size_t)C::WAVES * C::RPW * kRing * 4;
+         (size_t)C::WAVES * C::RPW * kRing * 4 + kSinkBytes;
 }
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -81,65 +85,59 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   float *dsc = reinterpret_cast<float *>(lds + (size_t)nwin * 1024);  // nb + 2
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = wave_id();
   float *stab = dsc + (nb + 2) + wave * RPW * kRing;  // RPW rings of kRing floats
   const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
-  const int8_t *qa = qs + (int64_t)t * in_f;
-  const float *da = d + (int64_t)t * nb;
+  const rsrc_t qrs = buf_rsrc(qs + (int64_t)t * in_f, (uint32_t)in_f);
+  const rsrc_t drs = buf_rsrc(d + (int64_t)t * nb, (uint32_t)nb * 4);
 
-  // 1. this thread's activation blocks and scales (oldest loads).
+  // 1. this thread's activation blocks and scales (oldest loads; zeros past the row).
   int4_t aq[KQ][2];
   float dv[KD];
 #pragma unroll
   for (int k = 0; k < KQ; ++k) {
-    const int b = threadIdx.x + k * NTH;
-    aq[k][0] = aq[k][1] = (int4_t){0, 0, 0, 0};
-    if (b < nb) {
-      aq[k][0] = *reinterpret_cast<const int4_t *>(qa + 32 * b);
-      aq[k][1] = *reinterpret_cast<const int4_t *>(qa + 32 * b + 16);
-    }
+    const uint32_t off = (uint32_t)(threadIdx.x + k * NTH) * 32;
+    aq[k][0] = buf_load16(qrs, off);
+    aq[k][1] = buf_load16(qrs, off + 16);
   }
 #pragma unroll
-  for (int k = 0; k < KD; ++k) {
-    const int b = threadIdx.x + k * NTH;
-    dv[k] = (b < nb) ? da[b] : 0.0f;
-  }
+  for (int k = 0; k < KD; ++k) dv[k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
 
-  // 2. the first batch of weight loads.
-  const uint8_t *wrow[RPW];
+  // 2. the first batch of weight loads: one resource per row over its nb * 34 used bytes (no
+  // bytes for a row past out_f), so chunks past the row read as zeros.
+  rsrc_t wrs[RPW];
   bool rok[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     rok[r] = rbase + r < out_f;
-    wrow[r] = W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + lane * 16;
+    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes,
+                      rok[r] ? (uint32_t)cpr * 16 : 0u);
   }
   int4_t wv[U][RPW];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      wv[u][r] = (int4_t){0, 0, 0, 0};
-      if (rok[r] && u * kWave + lane < cpr) wv[u][r] = load_stream16(wrow[r] + u * 1024);
-    }
+    for (int r = 0; r < RPW; ++r)
+      wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)(u * 1024 + lane * 16));
   }
 
   // 3. stage the activation in the shape of a Q8_0 row -- per block two zero bytes where the
   // weight row has its fp16 scale, then the 32 qs -- with zeros past the row, and d_a.
   {
     uint16_t *sh16 = reinterpret_cast<uint16_t *>(shaped);
+    unsigned char *sink = lds + fast_lds_bytes<C>(in_f) - kSinkBytes;
 #pragma unroll
     for (int k = 0; k < KQ; ++k) {
       const int b = threadIdx.x + k * NTH;
-      if (b < nb) {
-        uint16_t *dst = sh16 + (kBlkBytes / 2) * b;  // 2-byte aligned
-        dst[0] = 0;
+      // 2-byte aligned block start, or the sink for a thread past the last block.
+      uint16_t *dst = b < nb ? sh16 + (kBlkBytes / 2) * b : reinterpret_cast<uint16_t *>(sink);
+      dst[0] = 0;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            dst[1 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] & 0xFFFFu);
-            dst[2 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] >> 16);
-          }
+        for (int j = 0; j < 4; ++j) {
+          dst[1 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] & 0xFFFFu);
+          dst[2 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] >> 16);
         }
       }
     }
@@ -147,7 +145,8 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
       const int b = threadIdx.x + k * NTH;
-      if (b < nb + 2) dsc[b] = dv[k];
+      float *dst = b < nb + 2 ? dsc + b : reinterpret_cast<float *>(sink);
+      *dst = dv[k];
     }
   }
   __syncthreads();
@@ -203,17 +202,13 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
         acc[r] = fmaf((float)s_hi, S1, acc[r]);
       }
     }
+    // Next batch, issued unconditionally (past the row it reads zeros and no memory).
     const int nxt = w0 + U;
-    if (nxt < nwin) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          wv[u][r] = (int4_t){0, 0, 0, 0};
-          if (rok[r] && (nxt + u) * kWave + lane < cpr)
-            wv[u][r] = load_stream16(wrow[r] + (int64_t)(nxt + u) * 1024);
-        }
-      }
+      for (int r = 0; r < RPW; ++r)
+        wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)((nxt + u) * 1024 + lane * 16));
     }
   }
 
