@@ -142,7 +142,7 @@ def cpu_baseline(shapes, arms, threads: int):
 
 # ------------------------------------------------------------------ profile summaries
 PROFILES = os.path.join(ROOT, "profiles")
-PMC_SUMMARY = os.path.join(PROFILES, "gemv_hbm_counters.md")
+PMC_SUMMARY = os.path.join(PROFILES, "gemv_27b_shapes_hbm_counters.md")
 GEMV_SOURCES = ["fp8_gemv_amd/csrc/common.hpp", "fp8_gemv_amd/csrc/gemv_e4m3.hip",
                 "fp8_gemv_amd/csrc/gemv_q8_0.hip"]
 CALIB_MIB = 512
