@@ -19,6 +19,7 @@ constexpr int kQuadPerm1032 = 0xB1;  // lanes {1,0,3,2} within each quad
 constexpr int kQuadPerm2301 = 0x4E;  // lanes {2,3,0,1} within each quad
 constexpr int kRowRor4 = 0x124;      // rotate right by 4 within each row of 16
 constexpr int kRowRor8 = 0x128;      // rotate right by 8 within each row of 16
+constexpr int kWaveShr1 = 0x138;     // shift right by one lane across the whole wave
 
 // Full row and bank masks, bound_ctrl off: every lane has a valid source for these patterns.
 template <int CTRL>

@@ -75,9 +75,12 @@ __device__ __forceinline__ float dot16(const int4_t w, const half2_t a[8]) {
 
 // Launch shape.  K chunks of 16 activation columns and KD block scales per thread cover the
 // whole activation row: K * WAVES * 1024 >= in_f and KD * WAVES * 64 >= in_f / 32.
-template <int WAVES_, int RPW_, int U_, int K_, int KD_>
+// DB: double-buffered window loop -- the next U windows are loaded before the current U are
+// consumed, so a wave never waits with nothing in flight (rows of many windows).
+template <int WAVES_, int RPW_, int U_, int K_, int KD_, bool DB_ = false>
 struct Cfg {
   static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, K = K_, KD = KD_;
+  static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = K * THREADS * 16;
 };
@@ -161,7 +164,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   float acc[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-  for (int w0 = 0; w0 < nwin; w0 += U) {
+  auto compute = [&](const int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
@@ -172,16 +175,32 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
         *reinterpret_cast<int4_t *>(a + 4) = *reinterpret_cast<const int4_t *>(act + col + 8);
         const float sc = dsc[col / 32];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r] = fmaf(dot16(wv[u][r], a), sc, acc[r]);
+        for (int r = 0; r < RPW; ++r) acc[r] = fmaf(dot16(wb[u][r], a), sc, acc[r]);
       }
     }
-    // Next batch, issued unconditionally (past the row it reads zeros and no memory).
-    const int nxt = w0 + U;
+  };
+  // Loads are issued unconditionally: past the row they read zeros and no memory.
+  auto load = [&](int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
-        wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)((nxt + u) * kWinCols + lane * 16));
+        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u) * kWinCols + lane * 16));
+    }
+  };
+  if constexpr (C::DB) {
+    int4_t wv2[U][RPW];
+    for (int w0 = 0; w0 < nwin; w0 += 2 * U) {
+      load(wv2, w0 + U);
+      compute(wv, w0);
+      if (w0 + U >= nwin) break;
+      load(wv, w0 + 2 * U);
+      compute(wv2, w0 + U);
+    }
+  } else {
+    for (int w0 = 0; w0 < nwin; w0 += U) {
+      compute(wv, w0);
+      load(wv, w0 + U);
     }
   }
 
@@ -212,12 +231,12 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
   return hipGetLastError();
 }
 
-// Shapes measured on MI355X: 4-wave workgroups with one row per wave and five windows in
-// flight up to in_f = 8192; 8 waves (so that the larger LDS row still allows 32 waves per CU)
-// up to 24576; 16 waves beyond.  All fit 64 VGPRs.
-using CfgSmall = Cfg<4, 1, 5, 2, 1>;   // in_f <= 8192
-using CfgMid = Cfg<8, 1, 5, 3, 2>;     // in_f <= 24576
-using CfgLarge = Cfg<16, 1, 5, 4, 4>;  // in_f <= 65536
+// Shapes measured on MI355X: 4-wave workgroups with one row per wave up to in_f = 8192; 8
+// waves (so that the larger LDS row still allows 32 waves per CU) up to 24576; 16 waves
+// beyond.  All double-buffer their windows (2 or 4 per batch) and fit 64 VGPRs.
+using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;   // in_f <= 8192
+using CfgMid = Cfg<8, 1, 4, 3, 2, true>;     // in_f <= 24576
+using CfgLarge = Cfg<16, 1, 4, 4, 4, true>;  // in_f <= 65536
 static_assert(CfgSmall::MAX_IN_F == 8192 && CfgMid::MAX_IN_F == 24576 &&
                   CfgLarge::MAX_IN_F == kMaxInF, "activation coverage");
 static_assert(CfgSmall::KD * CfgSmall::THREADS * 32 >= CfgSmall::MAX_IN_F &&

@@ -21,11 +21,11 @@
 //     the 2-byte scale sits between them), so a chunk's four dwords split into a prefix that
 //     belongs to block b0 and a suffix that belongs to b0 + 1; the two exact int32 sums are
 //     scaled separately.
-//   * A chunk contains at most one block scale.  The lane holding it converts it
-//     (fp16 -> f32, times the activation scale d_a[b]) and publishes it in a per-wave LDS
-//     ring of 64 entries indexed by block mod 64 (the blocks live at any one time span at
-//     most 33 consecutive indices); the lanes that need it read it back after a wave-local
-//     fence.
+//   * A chunk contains at most one block scale.  The lane holding it converts it (fp16 ->
+//     f32, times the activation scale d_a[b]).  The scale of a chunk's first block starts 0,
+//     1 or 2 chunks earlier -- 0, 1 or 2 lanes to the left -- so it reaches the lanes that
+//     need it through one or two wave-wide DPP right shifts; lanes 0 and 1 take lanes 62
+//     and 63 of the previous window, carried in scalar registers.  No LDS round trip.
 // Generic path (any in_f % 32 == 0): one lane per block, 2-byte loads; correct, not tuned.
 // Row t = blockIdx.y of the activation runs identical code, so each activation row of an
 // m-row call is bit-identical to an m=1 call on that row.
@@ -45,30 +45,34 @@ __host__ __device__ constexpr int windows_per_row(int in_f) {
 
 // Launch shape of the fast path.  Each thread stages KQ activation blocks and KD block scales:
 // KQ * WAVES * 64 >= in_f / 32 and KD * WAVES * 64 >= in_f / 32 + 2.
-template <int WAVES_, int RPW_, int U_, int KQ_, int KD_>
+// DB: double-buffered window loop -- the next U windows are loaded before the current U are
+// consumed, so a wave never waits with nothing in flight (rows of many windows).
+template <int WAVES_, int RPW_, int U_, int KQ_, int KD_, bool DB_ = false>
 struct QCfg {
   static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, KQ = KQ_, KD = KD_;
+  static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = KQ * THREADS * 32;
 };
 
-constexpr int kRing = 64;  // scale-ring entries per (wave, row)
-
-// LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2], then
-// one scale ring of kRing floats per (wave, row).
+// LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2].
 // Last: a 48-byte sink that takes the staging writes of threads with nothing to stage, so
 // that the staging code has no branches (a branch would let the compiler sink an activation
 // load behind the weight loads and then wait for all of them).
 constexpr size_t kSinkBytes = 48;
 template <class C>
 __host__ __device__ constexpr size_t fast_lds_bytes(int in_f) {
-  return (size_t)windows_per_row(in_f) * 1024 + (size_t)(in_f / 32 + 2) * 4 +
-         (size_t)C::WAVES * C::RPW * kRing * 4 + kSinkBytes;
+  return (size_t)windows_per_row(in_f) * 1024 + (size_t)(in_f / 32 + 2) * 4 + kSinkBytes;
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+// Wave-wide shift right by one lane (DPP wave_shr:1); lane 0 receives `in0`.
+__device__ __forceinline__ float wave_shr1(float v, float in0) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, in0),
+                                                               __builtin_bit_cast(int, v),
+                                                               kWaveShr1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
 template <class C>
@@ -86,7 +90,6 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
-  float *stab = dsc + (nb + 2) + wave * RPW * kRing;  // RPW rings of kRing floats
   const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
   const rsrc_t qrs = buf_rsrc(qs + (int64_t)t * in_f, (uint32_t)in_f);
   const rsrc_t drs = buf_rsrc(d + (int64_t)t * nb, (uint32_t)nb * 4);
@@ -151,11 +154,11 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   }
   __syncthreads();
 
-  float acc[RPW];
+  float acc[RPW], carry63[RPW], carry62[RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < RPW; ++r) acc[r] = carry63[r] = carry62[r] = 0.0f;
 
-  for (int w0 = 0; w0 < nwin; w0 += U) {
+  auto compute = [&](const int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
@@ -174,41 +177,56 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
       const int4_t a = *reinterpret_cast<const int4_t *>(shaped + p0);  // zero past the row
       const float da_h = dsc[live ? hb : 0];  // hb <= nb for a chunk inside the row
 
-      // Publish the scale that starts in this chunk: fp16 -> f32, times d_a.
+      // The scale that starts in this chunk (0 if none): fp16 -> f32, times d_a.  The scale of
+      // b0 sits delta = 0, 1 or 2 chunks back, i.e. delta lanes to the left: one or two
+      // wave-wide DPP right shifts, lanes 0 and 1 taking lanes 62 and 63 of the last window.
+      const int delta = o == 0 ? 0 : (o <= 16 ? 1 : 2);
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
-        if (has_scale) {
-          const int4_t w = wv[u][r];
-          const int q = hpos >> 2;
-          const uint32_t dw = q == 0 ? w[0] : (q == 1 ? w[1] : (q == 2 ? w[2] : w[3]));
-          const uint16_t hbits = (hpos & 2) ? (uint16_t)(dw >> 16) : (uint16_t)(dw & 0xFFFF);
-          stab[r * kRing + (hb % kRing)] = (float)__builtin_bit_cast(_Float16, hbits) * da_h;
-        }
-      }
-      wave_lds_fence();
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const int4_t w = wv[u][r];
+        const int4_t w = wb[u][r];
+        const int q = hpos >> 2;
+        const uint32_t dw = q == 0 ? w[0] : (q == 1 ? w[1] : (q == 2 ? w[2] : w[3]));
+        const uint16_t hbits = (hpos & 2) ? (uint16_t)(dw >> 16) : (uint16_t)(dw & 0xFFFF);
+        const float H = has_scale ? (float)__builtin_bit_cast(_Float16, hbits) * da_h : 0.0f;
+        const float h1 = wave_shr1(H, carry63[r]);   // scale of chunk c - 1
+        const float h2 = wave_shr1(h1, carry62[r]);  // scale of chunk c - 2
+        carry63[r] = lane_value(H, 63);
+        carry62[r] = lane_value(H, 62);
         const int t1 = __builtin_amdgcn_sdot4(w[0], a[0], 0, false);
         const int t2 = __builtin_amdgcn_sdot4(w[1], a[1], t1, false);
         const int t3 = __builtin_amdgcn_sdot4(w[2], a[2], t2, false);
         const int t4 = __builtin_amdgcn_sdot4(w[3], a[3], t3, false);
         const int s_lo = nlo == 4 ? t4 : (nlo == 3 ? t3 : (nlo == 2 ? t2 : t1));
         const int s_hi = t4 - s_lo;
-        const float *tab = stab + r * kRing;
-        const float S0 = live ? tab[b0 % kRing] : 0.0f;
-        const float S1 = (live && nlo < 4) ? tab[(b0 + 1) % kRing] : 0.0f;
+        const float S0 = live ? (delta == 0 ? H : (delta == 1 ? h1 : h2)) : 0.0f;
+        const float S1 = (live && nlo < 4) ? H : 0.0f;
         acc[r] = fmaf((float)s_lo, S0, acc[r]);
         acc[r] = fmaf((float)s_hi, S1, acc[r]);
       }
     }
-    // Next batch, issued unconditionally (past the row it reads zeros and no memory).
-    const int nxt = w0 + U;
+  };
+  // Loads are issued unconditionally: past the row they read zeros and no memory.
+  auto load = [&](int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
-        wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)((nxt + u) * 1024 + lane * 16));
+        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u) * 1024 + lane * 16));
+    }
+  };
+  if constexpr (C::DB) {
+    int4_t wv2[U][RPW];
+    for (int w0 = 0; w0 < nwin; w0 += 2 * U) {
+      load(wv2, w0 + U);
+      compute(wv, w0);
+      if (w0 + U >= nwin) break;
+      load(wv, w0 + 2 * U);
+      compute(wv2, w0 + U);
+    }
+  } else {
+    for (int w0 = 0; w0 < nwin; w0 += U) {
+      compute(wv, w0);
+      load(wv, w0 + U);
     }
   }
 
@@ -269,11 +287,12 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
   return hipGetLastError();
 }
 
-// Shapes as for the e4m3 stream: 4 waves up to in_f = 8192, 8 up to 24576, 16 beyond; a row
-// of in_f = 5120 is 6 windows (the last one partly used), so U = 6 covers it in one batch.
-using QSmall = QCfg<4, 1, 6, 1, 2>;   // in_f <= 8192
-using QMid = QCfg<8, 1, 6, 2, 3>;     // in_f <= 32768
-using QLarge = QCfg<16, 1, 6, 2, 3>;  // in_f <= 65536
+// Shapes as for the e4m3 stream: 4 waves up to in_f = 8192, 8 up to 24576, 16 beyond, with
+// double-buffered batches of 3 or 4 windows (a row of in_f = 5120 is 6 windows, the last one
+// partly used).
+using QSmall = QCfg<4, 1, 3, 1, 2, true>;   // in_f <= 8192
+using QMid = QCfg<8, 1, 4, 2, 3, true>;     // in_f <= 32768
+using QLarge = QCfg<16, 1, 4, 2, 3, true>;  // in_f <= 65536
 static_assert(QLarge::MAX_IN_F == kMaxInF, "activation coverage");
 static_assert(QSmall::KD * QSmall::THREADS >= QSmall::MAX_IN_F / 32 + 2 &&
                   QMid::KD * QMid::THREADS >= QMid::MAX_IN_F / 32 + 2 &&
