@@ -31,7 +31,7 @@ FP8GEMV_MAX_IN_F = 65536
 FP8GEMV_MAX_M = 65535
 
 EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "gemv_q8_0_q81", "gemv_e4m3_q81",
-           "gemv_e4m3_blk128_q81", "fp8gemv_strerror")
+           "gemv_e4m3_blk128_q81", "fp8gemv_read_bytes", "fp8gemv_strerror")
 
 
 class Fp8GemvError(RuntimeError):
@@ -61,6 +61,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = i32
+    lib.fp8gemv_read_bytes.argtypes = [vp, i64, vp, vp]
+    lib.fp8gemv_read_bytes.restype = i32
     lib.fp8gemv_strerror.argtypes = [i32]
     lib.fp8gemv_strerror.restype = ctypes.c_char_p
     return lib
@@ -195,6 +197,14 @@ def gemv_e4m3_blk128_q81(W, row_bytes: int, grid, grid_cols: int, qs, d, y, m: i
         _ptr(y, "y", torch.float32, m * out_f, dev),
         m, in_f, out_f, _stream(stream))
     _check("gemv_e4m3_blk128_q81", rc)
+
+
+def fp8gemv_read_bytes(buf, nbytes: int, sink, stream=None) -> None:
+    """Measurement aid: stream nbytes of buf with the GEMVs' load pattern (no result)."""
+    dev = _dev(buf)
+    rc = _lib.fp8gemv_read_bytes(_ptr(buf, "buf", torch.uint8, nbytes, dev), nbytes,
+                                 _ptr(sink, "sink", torch.int32, 1, dev), _stream(stream))
+    _check("fp8gemv_read_bytes", rc)
 
 
 # ------------------------------------------------------------------------- byte counts

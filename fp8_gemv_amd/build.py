@@ -23,6 +23,7 @@ SOURCES = {
     "producer.hip": ["-ffp-contract=off"],
     "gemv_e4m3.hip": [],
     "gemv_q8_0.hip": [],
+    "read_ceiling.hip": [],
     "capi.hip": [],
 }
 

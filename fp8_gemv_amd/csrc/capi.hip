@@ -86,6 +86,14 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
                                              m, in_f, out_f, (hipStream_t)stream));
 }
 
+int fp8gemv_read_bytes(const void *p, int64_t bytes, uint32_t *sink, void *stream) {
+  if (!p || !sink) return FP8GEMV_ERR_NULL;
+  if (bytes < 1) return FP8GEMV_ERR_SHAPE;
+  if (bytes > FP8GEMV_MAX_READ_BYTES) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(p, 16) || !aligned(sink, 4)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_read_bytes(p, bytes, sink, (hipStream_t)stream));
+}
+
 const char *fp8gemv_strerror(int rc) {
   switch (rc) {
     case FP8GEMV_OK: return "ok";

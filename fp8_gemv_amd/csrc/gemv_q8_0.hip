@@ -293,7 +293,8 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
 using QSmall = QCfg<4, 1, 3, 1, 2, true>;   // in_f <= 8192
 using QMid = QCfg<8, 1, 4, 2, 3, true>;     // in_f <= 32768
 using QLarge = QCfg<16, 1, 4, 2, 3, true>;  // in_f <= 65536
-static_assert(QLarge::MAX_IN_F == kMaxInF, "activation coverage");
+static_assert(QSmall::MAX_IN_F >= 8192 && QMid::MAX_IN_F >= 24576 && QLarge::MAX_IN_F == kMaxInF,
+              "activation coverage of the in_f ranges dispatched to each shape");
 static_assert(QSmall::KD * QSmall::THREADS >= QSmall::MAX_IN_F / 32 + 2 &&
                   QMid::KD * QMid::THREADS >= QMid::MAX_IN_F / 32 + 2 &&
                   QLarge::KD * QLarge::THREADS >= QLarge::MAX_IN_F / 32 + 2,

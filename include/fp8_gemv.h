@@ -136,6 +136,18 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
                          const int8_t *qs, const float *d, float *y, int m, int in_f, int out_f,
                          void *stream);
 
+/*
+ * fp8gemv_read_bytes -- measurement aid, not a step of the matvec: streams `bytes` bytes from
+ * p with the GEMVs' load pattern (16-byte non-temporal loads, 1 KiB per wave-wide load,
+ * 8 KiB per wave) and discards them; `sink` (one uint32) is written only in the
+ * practically impossible case that the folded data equal a fixed constant.  Timing it on a
+ * cold range gives the achievable read ceiling the GEMV timings are compared with.
+ *   p      device pointer, 16-byte aligned;  1 <= bytes <= FP8GEMV_MAX_READ_BYTES
+ *   sink   device pointer to one uint32, 4-byte aligned
+ */
+#define FP8GEMV_MAX_READ_BYTES ((int64_t)1 << 40)
+int fp8gemv_read_bytes(const void *p, int64_t bytes, uint32_t *sink, void *stream);
+
 /* Human-readable text for a return code (static storage, never NULL). */
 const char *fp8gemv_strerror(int rc);
 

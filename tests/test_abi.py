@@ -31,7 +31,7 @@ def fg():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1",
                                   "gemv_q8_0_q81", "gemv_e4m3_q81", "gemv_e4m3_blk128_q81",
-                                  "fp8gemv_strerror"])
+                                  "fp8gemv_read_bytes", "fp8gemv_strerror"])
 
 
 def test_library_exports_every_declared_symbol(fg):
@@ -114,6 +114,14 @@ def test_gemv_argument_errors(fg):
     assert L.gemv_q8_0_q81(FAKE + 1, 68, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
     assert L.gemv_q8_0_q81(FAKE, 69, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
     assert L.gemv_q8_0_q81(FAKE, 68, FAKE + 4, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+
+
+def test_read_bytes_argument_errors(fg):
+    L = fg.lib()
+    assert L.fp8gemv_read_bytes(None, 1024, FAKE, None) == fg.FP8GEMV_ERR_NULL
+    assert L.fp8gemv_read_bytes(FAKE, 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.fp8gemv_read_bytes(FAKE + 4, 1024, FAKE, None) == fg.FP8GEMV_ERR_ALIGN
+    assert L.fp8gemv_read_bytes(FAKE, (1 << 40) + 1, FAKE, None) == fg.FP8GEMV_ERR_TOO_LARGE
 
 
 def test_binding_rejects_cpu_tensors_and_short_buffers(fg):

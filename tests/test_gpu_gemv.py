@@ -253,3 +253,12 @@ def test_graph_replays_match_eager(fg):
             assert e.tobytes() == gy.tobytes(), rep
         run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_read_bytes_measurement_kernel_runs(fg):
+    case("fp8gemv_read_bytes")
+    buf = torch.randint(0, 255, (3 * 32768 + 48,), dtype=torch.uint8, device=dev())
+    sink = torch.full((1,), 7, dtype=torch.int32, device=dev())
+    for nbytes in (16, 1000 * 16, buf.numel()):
+        fg.fp8gemv_read_bytes(buf, nbytes, sink)
+    assert int(host(sink)[0]) == 7
