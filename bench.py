@@ -169,8 +169,9 @@ def launch_signature(arm: str, out_f: int, in_f: int):
     """(kernel family, grid threads, workgroup size, LDS bytes) of the library's launch for
     one GEMV -- the launch-shape choice of the HIP library restated for labelling profiles."""
     waves = 4 if in_f <= 8192 else (8 if in_f <= 24576 else 16)
+    split = 2 if 8192 < in_f <= 24576 else 1  # waves sharing a row in the middle range
     wg = waves * 64
-    grid = -(-out_f // waves) * wg
+    grid = -(-out_f // (waves // split)) * wg
     if arm == "q8_0":
         nb = in_f // 32
         nwin = -(-(nb * 34 // 16) // 64)

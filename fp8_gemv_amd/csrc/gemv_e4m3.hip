@@ -77,20 +77,25 @@ __device__ __forceinline__ float dot16(const int4_t w, const half2_t a[8]) {
 // whole activation row: K * WAVES * 1024 >= in_f and KD * WAVES * 64 >= in_f / 32.
 // DB: double-buffered window loop -- the next U windows are loaded before the current U are
 // consumed, so a wave never waits with nothing in flight (rows of many windows).
-template <int WAVES_, int RPW_, int U_, int K_, int KD_, bool DB_ = false>
+template <int WAVES_, int RPW_, int U_, int K_, int KD_, bool DB_ = false, int WPE_ = 8,
+          int SPLIT_ = 1>
 struct Cfg {
-  static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, K = K_, KD = KD_;
+  static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, K = K_, KD = KD_, WPE = WPE_;
+  static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
+  static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
   static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = K * THREADS * 16;
 };
 
 template <bool BLK, class C>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
                  const float *__restrict__ grid, int grid_cols, const int8_t *__restrict__ qs,
                  const float *__restrict__ d, float *__restrict__ y, int in_f, int out_f) {
   constexpr int RPW = C::RPW, U = C::U, K = C::K, KD = C::KD, NTH = C::THREADS;
+  constexpr int SPLIT = C::SPLIT;
+  static_assert(C::WAVES % SPLIT == 0 && 128 % C::ROWS == 0, "a workgroup's rows lie in one tile");
   extern __shared__ __align__(16) unsigned char lds[];
   const int nwin = num_windows(in_f);
   _Float16 *act = reinterpret_cast<_Float16 *>(lds);
@@ -99,7 +104,9 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
-  const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
+  const int rbase = (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
+  const int part = wave % SPLIT;
+  const int wbeg = part * nwin / SPLIT, wend = (part + 1) * nwin / SPLIT;  // this wave's windows
   const int nb = in_f / 32;
   const rsrc_t qrs = buf_rsrc(qs + (int64_t)t * in_f, (uint32_t)in_f);
   const rsrc_t drs = buf_rsrc(d + (int64_t)t * nb, (uint32_t)nb * 4);
@@ -114,7 +121,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   if (BLK) {
     // Grid row of this workgroup (its rows all lie in one 128-row tile); clamped so a
     // workgroup past the last row still reads inside the grid.
-    const int rfirst = blockIdx.x * C::WAVES * RPW;
+    const int rfirst = blockIdx.x * C::ROWS;
     const int grow = (rfirst < out_f ? rfirst : out_f - 1) / 128;
     const rsrc_t grs = buf_rsrc(grid + (int64_t)grow * grid_cols, (uint32_t)grid_cols * 4);
 #pragma unroll
@@ -128,8 +135,10 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     rok[r] = rbase + r < out_f;
-    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes,
-                      rok[r] ? (uint32_t)in_f : 0u);
+    // wbeg < nwin, so wbeg * 1024 < in_f and the record count is never negative
+    const int lim = in_f < wend * kWinCols ? in_f : wend * kWinCols;
+    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * kWinCols,
+                      rok[r] ? (uint32_t)(lim - wbeg * kWinCols) : 0u);
   }
   int4_t wv[U][RPW];
 #pragma unroll
@@ -168,7 +177,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
-      if (win < nwin) {
+      if (win < wend) {
         const int col = win * kWinCols + lane * 16;
         half2_t a[8];
         *reinterpret_cast<int4_t *>(a) = *reinterpret_cast<const int4_t *>(act + col);
@@ -185,29 +194,49 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
-        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u) * kWinCols + lane * 16));
+        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u - wbeg) * kWinCols + lane * 16));
     }
   };
   if constexpr (C::DB) {
     int4_t wv2[U][RPW];
-    for (int w0 = 0; w0 < nwin; w0 += 2 * U) {
+    for (int w0 = wbeg; w0 < wend; w0 += 2 * U) {
       load(wv2, w0 + U);
       compute(wv, w0);
-      if (w0 + U >= nwin) break;
+      if (w0 + U >= wend) break;
       load(wv, w0 + 2 * U);
       compute(wv2, w0 + U);
     }
   } else {
-    for (int w0 = 0; w0 < nwin; w0 += U) {
+    for (int w0 = wbeg; w0 < wend; w0 += U) {
       compute(wv, w0);
       load(wv, w0 + U);
     }
   }
 
+  if constexpr (SPLIT == 1) {
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float s = wave_sum(acc[r]);
-    if (lane == 0 && rok[r]) y[(int64_t)t * out_f + rbase + r] = BLK ? s : s * scale;
+    for (int r = 0; r < RPW; ++r) {
+      const float s = wave_sum(acc[r]);
+      if (lane == 0 && rok[r]) y[(int64_t)t * out_f + rbase + r] = BLK ? s : s * scale;
+    }
+  } else {
+    // the SPLIT partial sums of a row meet in LDS and are added in part order
+    __shared__ float psum[C::WAVES * RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float s = wave_sum(acc[r]);
+      if (lane == 0) psum[wave * RPW + r] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if (lane == 0 && part == 0 && rok[r]) {
+        float s = psum[wave * RPW + r];
+#pragma unroll
+        for (int p = 1; p < SPLIT; ++p) s += psum[(wave + p) * RPW + r];
+        y[(int64_t)t * out_f + rbase + r] = BLK ? s : s * scale;
+      }
+    }
   }
 }
 
@@ -224,20 +253,21 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int rows_per_wg = C::WAVES * C::RPW;
-  const dim3 g((out_f + rows_per_wg - 1) / rows_per_wg, m);
+  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, m);
   hipLaunchKernelGGL(kern, g, dim3(C::THREADS), act_lds_bytes(in_f) + kSinkBytes, s, W, row_bytes, scale,
                      grid, grid_cols, qs, d, y, in_f, out_f);
   return hipGetLastError();
 }
 
 // Shapes measured on MI355X: 4-wave workgroups with one row per wave up to in_f = 8192; 8
-// waves (so that the larger LDS row still allows 32 waves per CU) up to 24576; 16 waves
-// beyond.  All double-buffer their windows (2 or 4 per batch) and fit 64 VGPRs.
-using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;   // in_f <= 8192
-using CfgMid = Cfg<8, 1, 4, 3, 2, true>;     // in_f <= 24576
+// waves (so that the larger LDS row still allows 32 waves per CU) up to 24576, two waves
+// per row there (long rows, few of them: splitting keeps more, shorter-lived waves in
+// flight; 6% faster at 5120 x 17408); 16 waves beyond.  All double-buffer their windows
+// (2 to 4 per batch) and fit 64 VGPRs.
+using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;      // in_f <= 8192
+using CfgMid = Cfg<8, 1, 3, 3, 2, true, 8, 2>;  // in_f <= 24576
 using CfgLarge = Cfg<16, 1, 4, 4, 4, true>;  // in_f <= 65536
-static_assert(CfgSmall::MAX_IN_F == 8192 && CfgMid::MAX_IN_F == 24576 &&
+static_assert(CfgSmall::MAX_IN_F == 8192 && CfgMid::MAX_IN_F >= 24576 &&
                   CfgLarge::MAX_IN_F == kMaxInF, "activation coverage");
 static_assert(CfgSmall::KD * CfgSmall::THREADS * 32 >= CfgSmall::MAX_IN_F &&
                   CfgMid::KD * CfgMid::THREADS * 32 >= CfgMid::MAX_IN_F &&

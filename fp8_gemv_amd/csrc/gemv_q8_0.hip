@@ -47,9 +47,12 @@ __host__ __device__ constexpr int windows_per_row(int in_f) {
 // KQ * WAVES * 64 >= in_f / 32 and KD * WAVES * 64 >= in_f / 32 + 2.
 // DB: double-buffered window loop -- the next U windows are loaded before the current U are
 // consumed, so a wave never waits with nothing in flight (rows of many windows).
-template <int WAVES_, int RPW_, int U_, int KQ_, int KD_, bool DB_ = false>
+template <int WAVES_, int RPW_, int U_, int KQ_, int KD_, bool DB_ = false, int WPE_ = 8,
+          int SPLIT_ = 1>
 struct QCfg {
-  static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, KQ = KQ_, KD = KD_;
+  static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, KQ = KQ_, KD = KD_, WPE = WPE_;
+  static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
+  static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
   static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = KQ * THREADS * 32;
@@ -76,11 +79,13 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
                       const int8_t *__restrict__ qs, const float *__restrict__ d,
                       float *__restrict__ y, int in_f, int out_f) {
   constexpr int RPW = C::RPW, U = C::U, KQ = C::KQ, KD = C::KD, NTH = C::THREADS;
+  constexpr int SPLIT = C::SPLIT;
+  static_assert(C::WAVES % SPLIT == 0, "whole row groups per workgroup");
   extern __shared__ __align__(16) unsigned char lds[];
   const int nb = in_f / 32;
   const int cpr = chunks_per_row(in_f);
@@ -90,7 +95,9 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
-  const int rbase = (blockIdx.x * C::WAVES + wave) * RPW;
+  const int rbase = (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
+  const int part = wave % SPLIT;
+  const int wbeg = part * nwin / SPLIT, wend = (part + 1) * nwin / SPLIT;  // this wave's windows
   const rsrc_t qrs = buf_rsrc(qs + (int64_t)t * in_f, (uint32_t)in_f);
   const rsrc_t drs = buf_rsrc(d + (int64_t)t * nb, (uint32_t)nb * 4);
 
@@ -106,15 +113,37 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
 #pragma unroll
   for (int k = 0; k < KD; ++k) dv[k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
 
-  // 2. the first batch of weight loads: one resource per row over its nb * 34 used bytes (no
-  // bytes for a row past out_f), so chunks past the row read as zeros.
+  // 2. the first batch of weight loads: one resource per row over the used bytes of this
+  // wave's windows (none for a row past out_f), so chunks past them read as zeros.
   rsrc_t wrs[RPW];
   bool rok[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     rok[r] = rbase + r < out_f;
-    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes,
-                      rok[r] ? (uint32_t)cpr * 16 : 0u);
+    // wbeg < nwin, so 1024 * wbeg < 16 * cpr and the record count is never negative
+    const int lim = cpr * 16 < wend * 1024 ? cpr * 16 : wend * 1024;
+    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * 1024,
+                      rok[r] ? (uint32_t)(lim - wbeg * 1024) : 0u);
+  }
+  // A wave that starts inside the row (wbeg > 0) also needs the block scales that lanes 62
+  // and 63 of window wbeg - 1 would carry into it: those two lanes fetch the two scale bytes
+  // of their chunk of that window, if it holds one (every other lane reads past the resource,
+  // i.e. zero, without touching memory).
+  uint32_t prev_bits[RPW];
+  const int pc = (wbeg - 1) * kWave + lane;  // chunk of window wbeg - 1 (used when wbeg > 0)
+  const int pb = 16 * pc / kBlkBytes;
+  const int phb = pb + (16 * pc - kBlkBytes * pb != 0);
+  const int phpos = kBlkBytes * phb - 16 * pc;
+  const bool prev_scale = SPLIT > 1 && wbeg > 0 && lane >= kWave - 2 && phpos <= 14;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    prev_bits[r] = 0;
+    if constexpr (SPLIT > 1) {
+      const rsrc_t rowrs = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes,
+                                    rok[r] ? (uint32_t)cpr * 16 : 0u);
+      prev_bits[r] = __builtin_amdgcn_raw_buffer_load_b16(
+          rowrs, prev_scale ? (uint32_t)(16 * pc + phpos) : (uint32_t)cpr * 16, 0, 0);
+    }
   }
   int4_t wv[U][RPW];
 #pragma unroll
@@ -156,13 +185,21 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
 
   float acc[RPW], carry63[RPW], carry62[RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = carry63[r] = carry62[r] = 0.0f;
+  for (int r = 0; r < RPW; ++r) {
+    acc[r] = 0.0f;
+    // the same value lanes 62 and 63 compute for window wbeg - 1 (zero at the row start)
+    const float H = prev_scale ? (float)__builtin_bit_cast(_Float16, (uint16_t)prev_bits[r]) *
+                                     dsc[prev_scale ? phb : 0]
+                               : 0.0f;
+    carry63[r] = lane_value(H, 63);
+    carry62[r] = lane_value(H, 62);
+  }
 
   auto compute = [&](const int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
-      if (win >= nwin) break;
+      if (win >= wend) break;
       const int c = win * kWave + lane;  // chunk index within the row
       const bool live = c < cpr;
       // Chunk geometry (the same for every row): bytes [p0, p0 + 16) of the row.
@@ -211,29 +248,49 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
-        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u) * 1024 + lane * 16));
+        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u - wbeg) * 1024 + lane * 16));
     }
   };
   if constexpr (C::DB) {
     int4_t wv2[U][RPW];
-    for (int w0 = 0; w0 < nwin; w0 += 2 * U) {
+    for (int w0 = wbeg; w0 < wend; w0 += 2 * U) {
       load(wv2, w0 + U);
       compute(wv, w0);
-      if (w0 + U >= nwin) break;
+      if (w0 + U >= wend) break;
       load(wv, w0 + 2 * U);
       compute(wv2, w0 + U);
     }
   } else {
-    for (int w0 = 0; w0 < nwin; w0 += U) {
+    for (int w0 = wbeg; w0 < wend; w0 += U) {
       compute(wv, w0);
       load(wv, w0 + U);
     }
   }
 
+  if constexpr (SPLIT == 1) {
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float s = wave_sum(acc[r]);
-    if (lane == 0 && rok[r]) y[(int64_t)t * out_f + rbase + r] = s;
+    for (int r = 0; r < RPW; ++r) {
+      const float s = wave_sum(acc[r]);
+      if (lane == 0 && rok[r]) y[(int64_t)t * out_f + rbase + r] = s;
+    }
+  } else {
+    // the SPLIT partial sums of a row meet in LDS and are added in part order
+    __shared__ float psum[C::WAVES * RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float s = wave_sum(acc[r]);
+      if (lane == 0) psum[wave * RPW + r] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if (lane == 0 && part == 0 && rok[r]) {
+        float s = psum[wave * RPW + r];
+#pragma unroll
+        for (int p = 1; p < SPLIT; ++p) s += psum[(wave + p) * RPW + r];
+        y[(int64_t)t * out_f + rbase + r] = s;
+      }
+    }
   }
 }
 
@@ -280,8 +337,7 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int rows_per_wg = C::WAVES * C::RPW;
-  const dim3 g((out_f + rows_per_wg - 1) / rows_per_wg, m);
+  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, m);
   hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes<C>(in_f), s, W, row_bytes, qs, d,
                      y, in_f, out_f);
   return hipGetLastError();
@@ -289,9 +345,11 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
 
 // Shapes as for the e4m3 stream: 4 waves up to in_f = 8192, 8 up to 24576, 16 beyond, with
 // double-buffered batches of 3 or 4 windows (a row of in_f = 5120 is 6 windows, the last one
-// partly used).
-using QSmall = QCfg<4, 1, 3, 1, 2, true>;   // in_f <= 8192
-using QMid = QCfg<8, 1, 4, 2, 3, true>;     // in_f <= 32768
+// partly used).  In the middle range two waves share each row (4 rows per workgroup): rows
+// of 17408 columns are 19 windows, and with one wave per row a 5120-row matrix would keep
+// only 20 long-lived waves per CU, unevenly spread; measured 10% faster split.
+using QSmall = QCfg<4, 1, 3, 1, 2, true>;         // in_f <= 8192
+using QMid = QCfg<8, 1, 4, 2, 3, true, 8, 2>;     // in_f <= 32768
 using QLarge = QCfg<16, 1, 4, 2, 3, true>;  // in_f <= 65536
 static_assert(QSmall::MAX_IN_F >= 8192 && QMid::MAX_IN_F >= 24576 && QLarge::MAX_IN_F == kMaxInF,
               "activation coverage of the in_f ranges dispatched to each shape");

@@ -81,8 +81,12 @@ def _assert_close(y, yo, A, rows=None):
 # Shapes [out_f, in_f] from a single window to several, with ragged tails in both directions
 # (in_f not a multiple of the 1 KiB window or of 256, out_f not a multiple of the 8 rows per
 # workgroup or of the 128-row grid tile).
+# Beyond in_f = 8192 two waves share a row, the second starting mid-row: 8704 puts the Q8_0
+# split where the first block's scale lies two chunks back in the first wave's last window,
+# 8224 leaves a 32-column last window, 9600 is not a multiple of 256 (Q8_0 generic path),
+# 24576 is the largest in_f of that launch shape.
 SMALL = [(1, 32), (7, 96), (130, 160), (131, 288), (257, 1056), (300, 2080), (64, 4096),
-         (129, 4352), (33, 1280), (250, 2048)]
+         (129, 4352), (33, 1280), (250, 2048), (37, 8704), (5, 8224), (131, 9600), (9, 24576)]
 
 
 @pytest.mark.parametrize("m", [1, 3])
@@ -114,9 +118,9 @@ def test_gemv_full_shapes_sampled_rows(fg, kind, out_f, in_f):
         _assert_close(y, yo, A, rows)
 
 
+@pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("kind", KINDS)
-def test_gemv_m_rows_bit_identical_to_m1(fg, kind):
-    out_f, in_f = 17408, 5120
+def test_gemv_m_rows_bit_identical_to_m1(fg, kind, out_f, in_f):
     c = Case(kind, out_f, in_f, 8)
     for m in (1, 2, 4, 8):
         case(f"{kind} m={m} out_f={out_f} in_f={in_f}")
