@@ -173,9 +173,8 @@ def launch_signature(arm: str, out_f: int, in_f: int):
     wg = waves * 64
     grid = -(-out_f // (waves // split)) * wg
     if arm == "q8_0":
-        nb = in_f // 32
-        nwin = -(-(nb * 34 // 16) // 64)
-        lds = nwin * 1024 + (nb + 2) * 4 + 48
+        nwin = -(-(in_f // 256) // 3)  # windows of 816 bytes (3 groups of 8 blocks)
+        lds = nwin * 816 + (nwin * 24 + 8) * 4 + 48
         return ("k_gemv_q8_0_fast", grid, wg, lds)
     lds = -(-in_f // 1024) * 2176 + 32
     return ("k_gemv_e4m3<true" if arm == "blk128" else "k_gemv_e4m3<false", grid, wg, lds)

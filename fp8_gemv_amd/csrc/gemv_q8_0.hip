@@ -9,10 +9,16 @@
 //
 // gfx950 design (the page's kernel is a CUDA warp-per-row MMVQ with dp4a; this one is not a
 // translation of it).  The difficulty is that 34-byte blocks do not line up with 16-byte
-// loads.  Fast path (in_f % 256 == 0, so every row is 17*in_f/256 whole 16-byte chunks and
-// every row starts the block pattern at a chunk boundary):
-//   * Lane l of a wave streams chunk 64*win + l of the row with one 16-byte non-temporal
-//     load: fully coalesced, every weight byte fetched exactly once.
+// loads.  Fast path (in_f % 256 == 0, W 16-byte aligned, row_bytes % 16 == 0):
+//   * The block pattern repeats every 272 bytes: a "group" is 8 blocks = 17 chunks of 16
+//     bytes, and every group starts on a block boundary.  A window is 3 groups (816 bytes):
+//     lane l < 51 streams chunk l of the window with one 16-byte non-temporal load, so a
+//     wave-wide load reads 816 contiguous bytes and every weight byte is fetched once; lanes
+//     51..63 load nothing (their offsets lie past the buffer resource).
+//   * Because windows start on group boundaries, everything about a lane's chunk -- where its
+//     block boundary falls, whether and where it holds a block scale, which lane holds the
+//     scale of its first block -- is the same in every window and every row.  It is worked
+//     out once per thread, outside the stream loop; per window only the data change.
 //   * The activation is staged in LDS "in the shape of a Q8_0 row": 34 bytes per block, two
 //     zero bytes where the weight row has its fp16 scale, then the 32 qs.  A weight chunk and
 //     the activation chunk at the same offset line up byte for byte, so four v_dot4_i32_i8
@@ -21,11 +27,12 @@
 //     the 2-byte scale sits between them), so a chunk's four dwords split into a prefix that
 //     belongs to block b0 and a suffix that belongs to b0 + 1; the two exact int32 sums are
 //     scaled separately.
-//   * A chunk contains at most one block scale.  The lane holding it converts it (fp16 ->
-//     f32, times the activation scale d_a[b]).  The scale of a chunk's first block starts 0,
-//     1 or 2 chunks earlier -- 0, 1 or 2 lanes to the left -- so it reaches the lanes that
-//     need it through one or two wave-wide DPP right shifts; lanes 0 and 1 take lanes 62
-//     and 63 of the previous window, carried in scalar registers.  No LDS round trip.
+//   * A chunk holds at most one block scale.  The lane holding it extracts the two bytes with
+//     v_perm_b32 (fixed selectors per lane), converts fp16 -> f32 and multiplies by d_a of
+//     that block.  The scale of a chunk's first block starts 0, 1 or 2 chunks earlier in the
+//     same group -- 0, 1 or 2 lanes to the left -- and reaches the lanes that need it through
+//     one or two wave-wide DPP right shifts.  A window never needs a value from the previous
+//     one, so a row can also be split between waves at any window.
 // Generic path (any in_f % 32 == 0): one lane per block, 2-byte loads; correct, not tuned.
 // Row t = blockIdx.y of the activation runs identical code, so each activation row of an
 // m-row call is bit-identical to an m=1 call on that row.
@@ -37,45 +44,49 @@ namespace {
 constexpr int kThreads = 256;  // generic path
 constexpr int kWaves = kThreads / kWave;
 constexpr int kBlkBytes = 34;
+constexpr int kGrpChunks = 17;                        // 272 bytes = 8 blocks = 256 weights
+constexpr int kWinLanes = 3 * kGrpChunks;             // 51 lanes stream a window
+constexpr int kWinBytes = kWinLanes * 16;             // 816 bytes
+constexpr int kWinBlocks = kWinBytes / kBlkBytes;     // 24 blocks
+static_assert(kWinBlocks * kBlkBytes == kWinBytes, "a window is whole blocks");
 
-__host__ __device__ constexpr int chunks_per_row(int in_f) { return in_f / 32 * kBlkBytes / 16; }
+// Windows of a row (fast path: in_f % 256 == 0, i.e. whole groups).
 __host__ __device__ constexpr int windows_per_row(int in_f) {
-  return (chunks_per_row(in_f) + kWave - 1) / kWave;
+  return (in_f / 256 + 2) / 3;
 }
 
 // Launch shape of the fast path.  Each thread stages KQ activation blocks and KD block scales:
-// KQ * WAVES * 64 >= in_f / 32 and KD * WAVES * 64 >= in_f / 32 + 2.
+// KQ * WAVES * 64 >= in_f / 32 and KD * WAVES * 64 >= in_f / 32 + 32 (the scale table is
+// padded with zeros to whole windows plus one group).
 // DB: double-buffered window loop -- the next U windows are loaded before the current U are
 // consumed, so a wave never waits with nothing in flight (rows of many windows).
 template <int WAVES_, int RPW_, int U_, int KQ_, int KD_, bool DB_ = false, int WPE_ = 8,
           int SPLIT_ = 1>
 struct QCfg {
   static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, KQ = KQ_, KD = KD_, WPE = WPE_;
+  static constexpr bool DB = DB_;
   static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
   static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
-  static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = KQ * THREADS * 32;
 };
 
-// LDS layout of the fast path: shaped activation (whole windows of 1 KiB), d_a[nb + 2].
-// Last: a 48-byte sink that takes the staging writes of threads with nothing to stage, so
-// that the staging code has no branches (a branch would let the compiler sink an activation
-// load behind the weight loads and then wait for all of them).
+// LDS layout of the fast path: shaped activation (whole windows), then d_a padded with zeros
+// to nwin * 24 + 8 entries.  Last: a 48-byte sink that takes the staging writes of threads
+// with nothing to stage, so that the staging code has no branches (a branch would let the
+// compiler sink an activation load behind the weight loads and then wait for all of them).
 constexpr size_t kSinkBytes = 48;
-template <class C>
+__host__ __device__ constexpr size_t dsc_entries(int in_f) {
+  return (size_t)windows_per_row(in_f) * kWinBlocks + 8;
+}
 __host__ __device__ constexpr size_t fast_lds_bytes(int in_f) {
-  return (size_t)windows_per_row(in_f) * 1024 + (size_t)(in_f / 32 + 2) * 4 + kSinkBytes;
+  return (size_t)windows_per_row(in_f) * kWinBytes + dsc_entries(in_f) * 4 + kSinkBytes;
 }
 
-// Wave-wide shift right by one lane (DPP wave_shr:1); lane 0 receives `in0`.
-__device__ __forceinline__ float wave_shr1(float v, float in0) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, in0),
-                                                               __builtin_bit_cast(int, v),
+// Wave-wide shift right by one lane (DPP wave_shr:1); lane 0 receives 0.
+__device__ __forceinline__ float wave_shr1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                kWaveShr1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane_value(float v, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
 template <class C>
@@ -88,10 +99,11 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   static_assert(C::WAVES % SPLIT == 0, "whole row groups per workgroup");
   extern __shared__ __align__(16) unsigned char lds[];
   const int nb = in_f / 32;
-  const int cpr = chunks_per_row(in_f);
+  const int row_used = nb * kBlkBytes;  // used bytes of a row (a multiple of 16)
   const int nwin = windows_per_row(in_f);
-  uint8_t *shaped = lds;                                              // nwin * 1024 bytes
-  float *dsc = reinterpret_cast<float *>(lds + (size_t)nwin * 1024);  // nb + 2
+  const int ndsc = nwin * kWinBlocks + 8;
+  uint8_t *shaped = lds;                                                   // nwin * 816 bytes
+  float *dsc = reinterpret_cast<float *>(lds + (size_t)nwin * kWinBytes);  // ndsc entries
   const int t = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
@@ -114,50 +126,33 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   for (int k = 0; k < KD; ++k) dv[k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
 
   // 2. the first batch of weight loads: one resource per row over the used bytes of this
-  // wave's windows (none for a row past out_f), so chunks past them read as zeros.
+  // wave's windows (none for a row past out_f), so chunks past them read as zeros.  Lanes
+  // 51..63 use an offset past any resource.
+  const uint32_t lane_off = lane < kWinLanes ? (uint32_t)lane * 16 : 0x40000000u;
   rsrc_t wrs[RPW];
   bool rok[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     rok[r] = rbase + r < out_f;
-    // wbeg < nwin, so 1024 * wbeg < 16 * cpr and the record count is never negative
-    const int lim = cpr * 16 < wend * 1024 ? cpr * 16 : wend * 1024;
-    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * 1024,
-                      rok[r] ? (uint32_t)(lim - wbeg * 1024) : 0u);
-  }
-  // A wave that starts inside the row (wbeg > 0) also needs the block scales that lanes 62
-  // and 63 of window wbeg - 1 would carry into it: those two lanes fetch the two scale bytes
-  // of their chunk of that window, if it holds one (every other lane reads past the resource,
-  // i.e. zero, without touching memory).
-  uint32_t prev_bits[RPW];
-  const int pc = (wbeg - 1) * kWave + lane;  // chunk of window wbeg - 1 (used when wbeg > 0)
-  const int pb = 16 * pc / kBlkBytes;
-  const int phb = pb + (16 * pc - kBlkBytes * pb != 0);
-  const int phpos = kBlkBytes * phb - 16 * pc;
-  const bool prev_scale = SPLIT > 1 && wbeg > 0 && lane >= kWave - 2 && phpos <= 14;
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    prev_bits[r] = 0;
-    if constexpr (SPLIT > 1) {
-      const rsrc_t rowrs = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes,
-                                    rok[r] ? (uint32_t)cpr * 16 : 0u);
-      prev_bits[r] = __builtin_amdgcn_raw_buffer_load_b16(
-          rowrs, prev_scale ? (uint32_t)(16 * pc + phpos) : (uint32_t)cpr * 16, 0, 0);
-    }
+    // wbeg < nwin, so 816 * wbeg < row_used and the record count is never negative
+    const int lim = row_used < wend * kWinBytes ? row_used : wend * kWinBytes;
+    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * kWinBytes,
+                      rok[r] ? (uint32_t)(lim - wbeg * kWinBytes) : 0u);
   }
   int4_t wv[U][RPW];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
-      wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)(u * 1024 + lane * 16));
+      wv[u][r] = buf_load16_stream(wrs[r], lane_off + (uint32_t)(u * kWinBytes));
   }
 
   // 3. stage the activation in the shape of a Q8_0 row -- per block two zero bytes where the
-  // weight row has its fp16 scale, then the 32 qs -- with zeros past the row, and d_a.
+  // weight row has its fp16 scale, then the 32 qs -- with zeros to the end of the last
+  // window, and d_a with zeros past nb.
   {
     uint16_t *sh16 = reinterpret_cast<uint16_t *>(shaped);
-    unsigned char *sink = lds + fast_lds_bytes<C>(in_f) - kSinkBytes;
+    unsigned char *sink = lds + fast_lds_bytes(in_f) - kSinkBytes;
 #pragma unroll
     for (int k = 0; k < KQ; ++k) {
       const int b = threadIdx.x + k * NTH;
@@ -173,82 +168,78 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
         }
       }
     }
-    for (int i = (kBlkBytes / 2) * nb + threadIdx.x; i < nwin * 512; i += NTH) sh16[i] = 0;
+    for (int i = (kBlkBytes / 2) * nb + threadIdx.x; i < nwin * (kWinBytes / 2); i += NTH) sh16[i] = 0;
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
       const int b = threadIdx.x + k * NTH;
-      float *dst = b < nb + 2 ? dsc + b : reinterpret_cast<float *>(sink);
+      float *dst = b < ndsc ? dsc + b : reinterpret_cast<float *>(sink);
       *dst = dv[k];
     }
   }
+
+  // 4. this lane's chunk geometry, the same in every window: chunk r of group g of the window.
+  const int gidx = lane < kWinLanes ? lane / kGrpChunks : 0;
+  const int rch = lane < kWinLanes ? lane % kGrpChunks : kGrpChunks - 1;
+  const int p0 = 16 * rch;                 // byte offset of the chunk in its group
+  const int b0 = p0 / kBlkBytes;           // block of its first byte
+  const int o = p0 - kBlkBytes * b0;       // offset inside that block, even, 0..32
+  const int hb = b0 + (o != 0);            // block whose scale may start in the chunk
+  const int hpos = kBlkBytes * hb - p0;    // its byte offset inside the chunk
+  const bool has_scale = lane < kWinLanes && hpos <= 14;
+  // v_perm_b32 selectors that move the two scale bytes to bits 0..15 from dwords 0-1 or 2-3
+  // of the chunk; selector byte 0x0C yields zero, so a lane without a scale gets 0.
+  const uint32_t sel_lo = has_scale && hpos < 8
+                              ? 0x0C0C0000u | ((uint32_t)(hpos + 1) << 8) | (uint32_t)hpos
+                              : 0x0C0C0C0Cu;
+  const uint32_t sel_hi = has_scale && hpos >= 8
+                              ? 0x0C0C0000u | ((uint32_t)(hpos - 7) << 8) | (uint32_t)(hpos - 8)
+                              : 0x0C0C0C0Cu;
+  // dwords j < nlo hold quants of b0 (or its scale); the rest belong to b0 + 1.
+  const bool lo_ge2 = o <= 28, lo_ge3 = o <= 24, lo_4 = o <= 20;
+  // the scale of b0 sits delta = 0, 1 or 2 lanes to the left
+  const bool d0 = o == 0, d1 = o != 0 && o <= 16;
+  const int dsc_lane = 8 * gidx + (has_scale ? hb : 0);  // d_a entry of the scale, per window + 24
+  const int lds_lane = lane < kWinLanes ? lane * 16 : 0;  // lanes 51..63 multiply zero weights
   __syncthreads();
 
-  float acc[RPW], carry63[RPW], carry62[RPW];
+  float acc[RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    acc[r] = 0.0f;
-    // the same value lanes 62 and 63 compute for window wbeg - 1 (zero at the row start)
-    const float H = prev_scale ? (float)__builtin_bit_cast(_Float16, (uint16_t)prev_bits[r]) *
-                                     dsc[prev_scale ? phb : 0]
-                               : 0.0f;
-    carry63[r] = lane_value(H, 63);
-    carry62[r] = lane_value(H, 62);
-  }
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
 
   auto compute = [&](const int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
       if (win >= wend) break;
-      const int c = win * kWave + lane;  // chunk index within the row
-      const bool live = c < cpr;
-      // Chunk geometry (the same for every row): bytes [p0, p0 + 16) of the row.
-      const int p0 = 16 * c;
-      const int b0 = p0 / kBlkBytes;         // block of the first byte
-      const int o = p0 - kBlkBytes * b0;     // offset inside that block, even, 0..32
-      const int hb = b0 + (o != 0);          // block whose scale may start in the chunk
-      const int hpos = kBlkBytes * hb - p0;  // its byte offset inside the chunk
-      const bool has_scale = live && hpos <= 14;
-      // dwords j < nlo hold quants of b0 (or its scale); the rest belong to b0 + 1.
-      const int nlo = o <= 20 ? 4 : (o <= 24 ? 3 : (o <= 28 ? 2 : 1));
-      const int4_t a = *reinterpret_cast<const int4_t *>(shaped + p0);  // zero past the row
-      const float da_h = dsc[live ? hb : 0];  // hb <= nb for a chunk inside the row
-
-      // The scale that starts in this chunk (0 if none): fp16 -> f32, times d_a.  The scale of
-      // b0 sits delta = 0, 1 or 2 chunks back, i.e. delta lanes to the left: one or two
-      // wave-wide DPP right shifts, lanes 0 and 1 taking lanes 62 and 63 of the last window.
-      const int delta = o == 0 ? 0 : (o <= 16 ? 1 : 2);
+      const int4_t a = *reinterpret_cast<const int4_t *>(shaped + win * kWinBytes + lds_lane);
+      const float da_h = dsc[win * kWinBlocks + dsc_lane];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const int4_t w = wb[u][r];
-        const int q = hpos >> 2;
-        const uint32_t dw = q == 0 ? w[0] : (q == 1 ? w[1] : (q == 2 ? w[2] : w[3]));
-        const uint16_t hbits = (hpos & 2) ? (uint16_t)(dw >> 16) : (uint16_t)(dw & 0xFFFF);
-        const float H = has_scale ? (float)__builtin_bit_cast(_Float16, hbits) * da_h : 0.0f;
-        const float h1 = wave_shr1(H, carry63[r]);   // scale of chunk c - 1
-        const float h2 = wave_shr1(h1, carry62[r]);  // scale of chunk c - 2
-        carry63[r] = lane_value(H, 63);
-        carry62[r] = lane_value(H, 62);
+        const uint32_t hbits = __builtin_amdgcn_perm((uint32_t)w[1], (uint32_t)w[0], sel_lo) |
+                               __builtin_amdgcn_perm((uint32_t)w[3], (uint32_t)w[2], sel_hi);
+        const float H = (float)__builtin_bit_cast(_Float16, (uint16_t)hbits) * da_h;
+        const float h1 = wave_shr1(H);   // scale of chunk c - 1
+        const float h2 = wave_shr1(h1);  // scale of chunk c - 2
         const int t1 = __builtin_amdgcn_sdot4(w[0], a[0], 0, false);
         const int t2 = __builtin_amdgcn_sdot4(w[1], a[1], t1, false);
         const int t3 = __builtin_amdgcn_sdot4(w[2], a[2], t2, false);
         const int t4 = __builtin_amdgcn_sdot4(w[3], a[3], t3, false);
-        const int s_lo = nlo == 4 ? t4 : (nlo == 3 ? t3 : (nlo == 2 ? t2 : t1));
+        const int s_lo = lo_4 ? t4 : (lo_ge3 ? t3 : (lo_ge2 ? t2 : t1));
         const int s_hi = t4 - s_lo;
-        const float S0 = live ? (delta == 0 ? H : (delta == 1 ? h1 : h2)) : 0.0f;
-        const float S1 = (live && nlo < 4) ? H : 0.0f;
+        const float S0 = d0 ? H : (d1 ? h1 : h2);
         acc[r] = fmaf((float)s_lo, S0, acc[r]);
-        acc[r] = fmaf((float)s_hi, S1, acc[r]);
+        acc[r] = fmaf((float)s_hi, H, acc[r]);
       }
     }
   };
-  // Loads are issued unconditionally: past the row they read zeros and no memory.
+  // Loads are issued unconditionally: past this wave's windows they read zeros and no memory.
   auto load = [&](int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
-        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u - wbeg) * 1024 + lane * 16));
+        wb[u][r] = buf_load16_stream(wrs[r], lane_off + (uint32_t)((w0 + u - wbeg) * kWinBytes));
     }
   };
   if constexpr (C::DB) {
@@ -333,29 +324,29 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)fast_lds_bytes<C>(C::MAX_IN_F));
+                                       (int)fast_lds_bytes(C::MAX_IN_F));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const dim3 g((out_f + C::ROWS - 1) / C::ROWS, m);
-  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes<C>(in_f), s, W, row_bytes, qs, d,
+  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes(in_f), s, W, row_bytes, qs, d,
                      y, in_f, out_f);
   return hipGetLastError();
 }
 
 // Shapes as for the e4m3 stream: 4 waves up to in_f = 8192, 8 up to 24576, 16 beyond, with
-// double-buffered batches of 3 or 4 windows (a row of in_f = 5120 is 6 windows, the last one
-// partly used).  In the middle range two waves share each row (4 rows per workgroup): rows
-// of 17408 columns are 19 windows, and with one wave per row a 5120-row matrix would keep
-// only 20 long-lived waves per CU, unevenly spread; measured 10% faster split.
+// double-buffered batches of 3 or 4 windows (a row of in_f = 5120 is 7 windows, the last one
+// two groups).  In the middle range two waves share each row (4 rows per workgroup): rows of
+// 17408 columns are 23 windows, and with one wave per row a 5120-row matrix would keep only
+// 20 long-lived waves per CU, unevenly spread.
 using QSmall = QCfg<4, 1, 3, 1, 2, true>;         // in_f <= 8192
 using QMid = QCfg<8, 1, 4, 2, 3, true, 8, 2>;     // in_f <= 32768
 using QLarge = QCfg<16, 1, 4, 2, 3, true>;  // in_f <= 65536
 static_assert(QSmall::MAX_IN_F >= 8192 && QMid::MAX_IN_F >= 24576 && QLarge::MAX_IN_F == kMaxInF,
               "activation coverage of the in_f ranges dispatched to each shape");
-static_assert(QSmall::KD * QSmall::THREADS >= QSmall::MAX_IN_F / 32 + 2 &&
-                  QMid::KD * QMid::THREADS >= QMid::MAX_IN_F / 32 + 2 &&
-                  QLarge::KD * QLarge::THREADS >= QLarge::MAX_IN_F / 32 + 2,
+static_assert(QSmall::KD * QSmall::THREADS >= (int)dsc_entries(QSmall::MAX_IN_F) &&
+                  QMid::KD * QMid::THREADS >= (int)dsc_entries(QMid::MAX_IN_F) &&
+                  QLarge::KD * QLarge::THREADS >= (int)dsc_entries(QLarge::MAX_IN_F),
               "scale coverage");
 
 }  // namespace

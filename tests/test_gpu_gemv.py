@@ -81,10 +81,10 @@ def _assert_close(y, yo, A, rows=None):
 # Shapes [out_f, in_f] from a single window to several, with ragged tails in both directions
 # (in_f not a multiple of the 1 KiB window or of 256, out_f not a multiple of the 8 rows per
 # workgroup or of the 128-row grid tile).
-# Beyond in_f = 8192 two waves share a row, the second starting mid-row: 8704 puts the Q8_0
-# split where the first block's scale lies two chunks back in the first wave's last window,
-# 8224 leaves a 32-column last window, 9600 is not a multiple of 256 (Q8_0 generic path),
-# 24576 is the largest in_f of that launch shape.
+# Beyond in_f = 8192 two waves share a row, the second starting mid-row: 8704 and 24576 split
+# rows of an odd number of windows (Q8_0: 12 and 32 groups of 8 blocks, in windows of three
+# groups, the last one partial), 8224 leaves a 32-column last e4m3 window, 9600 is not a
+# multiple of 256 (Q8_0 generic path), 24576 is the largest in_f of that launch shape.
 SMALL = [(1, 32), (7, 96), (130, 160), (131, 288), (257, 1056), (300, 2080), (64, 4096),
          (129, 4352), (33, 1280), (250, 2048), (37, 8704), (5, 8224), (131, 9600), (9, 24576)]
 
