@@ -38,6 +38,9 @@ SHAPES = [(5120, 5120), (17408, 5120), (5120, 17408)]  # [out_f, in_f]
 ARMS = ["e4m3", "blk128", "q8_0"]
 SCALE = 2.0 ** -4
 EPS = 1e-6
+M_ROWS = (1, 2, 4, 8)   # small-batch activation rows, timed at SHAPE_M
+MAX_M = max(M_ROWS)
+SHAPE_M = (17408, 5120)
 
 
 def log(msg: str) -> None:
@@ -81,21 +84,21 @@ class Arm:
             g = torch.from_numpy(synth.blk128_grid(out_f, in_f)).to(dev)
             self.grids = [g] + [g.clone() for _ in range(self.copies - 1)]
             self.grid_cols = g.shape[1]
-        self.y = torch.empty(out_f, device=dev)
+        self.y = torch.empty(MAX_M * out_f, device=dev)
         self.i = 0
 
-    def launch(self, qs, d):
+    def launch(self, qs, d, m=1):
         c = self.i % self.copies
         self.i += 1
         fg = self.fg
         if self.arm == "q8_0":
-            fg.gemv_q8_0_q81(self.W[c], self.row_bytes, qs, d, self.y, 1, self.in_f, self.out_f)
+            fg.gemv_q8_0_q81(self.W[c], self.row_bytes, qs, d, self.y, m, self.in_f, self.out_f)
         elif self.arm == "e4m3":
-            fg.gemv_e4m3_q81(self.W[c], self.row_bytes, SCALE, qs, d, self.y, 1, self.in_f,
+            fg.gemv_e4m3_q81(self.W[c], self.row_bytes, SCALE, qs, d, self.y, m, self.in_f,
                              self.out_f)
         else:
             fg.gemv_e4m3_blk128_q81(self.W[c], self.row_bytes, self.grids[c], self.grid_cols, qs,
-                                    d, self.y, 1, self.in_f, self.out_f)
+                                    d, self.y, m, self.in_f, self.out_f)
 
 
 def cpu_baseline(shapes, arms, threads: int):
@@ -406,6 +409,31 @@ def main() -> int:
                 f.write(json.dumps({"arm": a, "out_f": out_f, "in_f": in_f,
                                     **detail[f"{a}@{out_f}x{in_f}"]}) + "\n")
 
+    # Small-batch rows (gemv_e4m3_bench.rs: m in {1, 2, 4, 8} through grid.y at 17408x5120):
+    # m activation rows from the producer with nrows = m, one GEMV call per launch, weights
+    # counted once per call.
+    m_rows = {}
+    if SHAPE_M in shapes and not args.kernels_only:
+        out_f, in_f = SHAPE_M
+        xm = torch.from_numpy(synth.x_rows(in_f, MAX_M)).to(dev)
+        wm = torch.from_numpy(synth.gain(in_f)).to(dev)
+        qsm = torch.empty(MAX_M * in_f, dtype=torch.int8, device=dev)
+        dm = torch.empty(MAX_M * (in_f // 32), device=dev)
+        fg.rmsnorm_q8_1(xm, wm, None, qsm, dm, in_f, MAX_M, EPS)
+        for a in arms:
+            obj = arm_objs[(out_f, in_f, a)]
+            for m in M_ROWS:
+                n = max(args.kernel_iters, obj.copies)
+                g = capture(lambda: [obj.launch(qsm, dm, m) for _ in range(n)])
+                g.replay()
+                us = timed(g.replay, n) * 1e3
+                wb = weight_bytes(a, out_f, in_f)
+                m_rows[f"{a}@{out_f}x{in_f}@m={m}"] = {
+                    "us": round(us, 3), "us_per_row": round(us / m, 3),
+                    "weight_GBs": round(wb / us / 1e3, 1),
+                    "alg_bytes": algorithmic_bytes(a, out_f, in_f, m)}
+                log(f"{a:7s} {out_f}x{in_f} m={m}: {us:8.2f} us  {us / m:7.2f} us/row")
+
     # Achievable read ceiling: the library's streaming-read measurement kernel over the same
     # rotated e4m3 copies (same bytes, same load pattern, no arithmetic).
     ceiling = {}
@@ -477,7 +505,7 @@ def main() -> int:
                    "eps": EPS, "e4m3_scale": SCALE},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
-        "gemv": detail, "read_ceiling": ceiling, "producer_us": prod_us,
+        "gemv": detail, "read_ceiling": ceiling, "m_rows": m_rows, "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

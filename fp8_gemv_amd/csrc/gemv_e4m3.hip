@@ -18,7 +18,9 @@
 //     (which waits only for the older activation loads) overlaps the weight stream instead of
 //     waiting behind it.
 //   * The q8_1 activation row is staged once per workgroup in LDS as f16 (int8 is exact in
-//     f16, converted with the 0x6400 exponent trick) next to its block scales -- for the
+//     f16, converted with the 0x6400 exponent trick; per window, the first 8 values of every
+//     lane's chunk and then the last 8, so LDS reads are contiguous across the wave) next
+//     to its block scales -- for the
 //     block-128 container the scale already times the grid value of the workgroup's
 //     128-row tile (all rows of a workgroup lie in one tile).
 //   * Decode: v_cvt_scalef32_pk_f16_fp8 turns two e4m3 bytes into two f16 with scale 1.0
@@ -48,6 +50,7 @@ __host__ __device__ constexpr size_t act_lds_bytes(int in_f) {
 // that the staging code has no branches (a branch would let the compiler sink an activation
 // load behind the weight loads and then wait for all of them).
 constexpr size_t kSinkBytes = 32;
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one CU, the most a workgroup may use
 
 // int8 x4 -> two f16 pairs, exactly: after flipping the sign bit a byte u is 0..255 and the
 // f16 with bits 0x6400 | u is 1024 + u; subtracting 1152 leaves the signed value.
@@ -60,16 +63,22 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t q, half2_t &lo, half2_t &hi
   hi = __builtin_bit_cast(half2_t, b) - off;
 }
 
-// 16-term dot of one lane's 16 e4m3 weights (one 16-byte load) with 16 staged f16 values.
-__device__ __forceinline__ float dot16(const int4_t w, const half2_t a[8]) {
-  float p = 0.0f;
+// One lane's 16 e4m3 weights (one 16-byte load) as 8 f16 pairs.  v_cvt_scalef32_pk_f16_fp8
+// with scale 1.0 is exact: every e4m3 value, subnormals included, is an f16 normal.
+__device__ __forceinline__ void decode16(const int4_t w, half2_t wh[8]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[j], 1.0f, false);
-    const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[j], 1.0f, true);
-    p = __builtin_amdgcn_fdot2(lo, a[2 * j], p, false);
-    p = __builtin_amdgcn_fdot2(hi, a[2 * j + 1], p, false);
+    wh[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[j], 1.0f, false);
+    wh[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[j], 1.0f, true);
   }
+}
+
+// 16-term dot of decoded weights with 16 staged f16 activation values, accumulated in f32 in
+// a fixed order (each product is exact: 4 + 8 significant bits).
+__device__ __forceinline__ float dot16(const half2_t wh[8], const half2_t a[8]) {
+  float p = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p = __builtin_amdgcn_fdot2(wh[j], a[j], p, false);
   return p;
 }
 
@@ -77,11 +86,14 @@ __device__ __forceinline__ float dot16(const int4_t w, const half2_t a[8]) {
 // whole activation row: K * WAVES * 1024 >= in_f and KD * WAVES * 64 >= in_f / 32.
 // DB: double-buffered window loop -- the next U windows are loaded before the current U are
 // consumed, so a wave never waits with nothing in flight (rows of many windows).
+// MT: activation rows per workgroup.  Each weight chunk is loaded and decoded once and used
+// for all MT rows; every row's arithmetic is exactly the MT = 1 sequence.
 template <int WAVES_, int RPW_, int U_, int K_, int KD_, bool DB_ = false, int WPE_ = 8,
-          int SPLIT_ = 1>
+          int SPLIT_ = 1, int MT_ = 1>
 struct Cfg {
   static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, K = K_, KD = KD_, WPE = WPE_;
   static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
+  static constexpr int MT = MT_;
   static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
   static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
@@ -92,32 +104,36 @@ template <bool BLK, class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
                  const float *__restrict__ grid, int grid_cols, const int8_t *__restrict__ qs,
-                 const float *__restrict__ d, float *__restrict__ y, int in_f, int out_f) {
-  constexpr int RPW = C::RPW, U = C::U, K = C::K, KD = C::KD, NTH = C::THREADS;
+                 const float *__restrict__ d, float *__restrict__ y, int m, int in_f, int out_f) {
+  constexpr int RPW = C::RPW, U = C::U, K = C::K, KD = C::KD, NTH = C::THREADS, MT = C::MT;
   constexpr int SPLIT = C::SPLIT;
   static_assert(C::WAVES % SPLIT == 0 && 128 % C::ROWS == 0, "a workgroup's rows lie in one tile");
   extern __shared__ __align__(16) unsigned char lds[];
   const int nwin = num_windows(in_f);
-  _Float16 *act = reinterpret_cast<_Float16 *>(lds);
-  float *dsc = reinterpret_cast<float *>(lds + (size_t)nwin * kWinCols * 2);
+  const size_t row_lds = act_lds_bytes(in_f);  // one staged activation row
 
-  const int t = blockIdx.y;
+  const int t0 = blockIdx.y * MT;  // first activation row of this workgroup
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
   const int rbase = (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
   const int part = wave % SPLIT;
   const int wbeg = part * nwin / SPLIT, wend = (part + 1) * nwin / SPLIT;  // this wave's windows
   const int nb = in_f / 32;
-  const rsrc_t qrs = buf_rsrc(qs + (int64_t)t * in_f, (uint32_t)in_f);
-  const rsrc_t drs = buf_rsrc(d + (int64_t)t * nb, (uint32_t)nb * 4);
 
-  // 1. this thread's share of the activation row (oldest loads; zeros past in_f).
-  int4_t aq[K];
-  float dv[KD];
+  // 1. this thread's share of the MT activation rows (oldest loads; zeros past in_f and for
+  // rows past m).
+  int4_t aq[MT][K];
+  float dv[MT][KD];
 #pragma unroll
-  for (int k = 0; k < K; ++k) aq[k] = buf_load16(qrs, (uint32_t)(threadIdx.x + k * NTH) * 16);
+  for (int tt = 0; tt < MT; ++tt) {
+    const bool tok = t0 + tt < m;
+    const rsrc_t qrs = buf_rsrc(qs + (int64_t)(tok ? t0 + tt : 0) * in_f, tok ? (uint32_t)in_f : 0u);
+    const rsrc_t drs = buf_rsrc(d + (int64_t)(tok ? t0 + tt : 0) * nb, tok ? (uint32_t)nb * 4 : 0u);
 #pragma unroll
-  for (int k = 0; k < KD; ++k) dv[k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
+    for (int k = 0; k < K; ++k) aq[tt][k] = buf_load16(qrs, (uint32_t)(threadIdx.x + k * NTH) * 16);
+#pragma unroll
+    for (int k = 0; k < KD; ++k) dv[tt][k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
+  }
   if (BLK) {
     // Grid row of this workgroup (its rows all lie in one 128-row tile); clamped so a
     // workgroup past the last row still reads inside the grid.
@@ -125,11 +141,15 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
     const int grow = (rfirst < out_f ? rfirst : out_f - 1) / 128;
     const rsrc_t grs = buf_rsrc(grid + (int64_t)grow * grid_cols, (uint32_t)grid_cols * 4);
 #pragma unroll
-    for (int k = 0; k < KD; ++k) dv[k] *= buf_load_f32(grs, (uint32_t)((threadIdx.x + k * NTH) / 4) * 4);
+    for (int k = 0; k < KD; ++k) {
+      const float gv = buf_load_f32(grs, (uint32_t)((threadIdx.x + k * NTH) / 4) * 4);
+#pragma unroll
+      for (int tt = 0; tt < MT; ++tt) dv[tt][k] *= gv;
+    }
   }
 
-  // 2. the first batch of weight loads: one resource per row over its first in_f bytes (no
-  // bytes for a row past out_f), so out-of-range windows and rows read as zeros.
+  // 2. the first batch of weight loads: one resource per row over this wave's windows of its
+  // first in_f bytes (none for a row past out_f), so out-of-range windows read as zeros.
   rsrc_t wrs[RPW];
   bool rok[RPW];
 #pragma unroll
@@ -148,43 +168,74 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
       wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)(u * kWinCols + lane * 16));
   }
 
-  // 3. stage the activation (f16) and its scales in LDS; zeros past in_f.  Threads past the
-  // staged range write into the sink instead of branching around the store.
-  unsigned char *sink = lds + act_lds_bytes(in_f);
+  // 3. stage the activation rows (f16) and their scales in LDS; zeros past in_f.  Threads
+  // past the staged range write into the sink instead of branching around the store.
+  unsigned char *sink = lds + MT * row_lds;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int c = (threadIdx.x + k * NTH) * 16;
-    half2_t h[8];
+  for (int tt = 0; tt < MT; ++tt) {
+    _Float16 *act = reinterpret_cast<_Float16 *>(lds + tt * row_lds);
+    float *dsc = reinterpret_cast<float *>(lds + tt * row_lds + (size_t)nwin * kWinCols * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) i8x4_to_f16((uint32_t)aq[k][j], h[2 * j], h[2 * j + 1]);
-    _Float16 *dst = c < nwin * kWinCols ? act + c : reinterpret_cast<_Float16 *>(sink);
-    *reinterpret_cast<int4_t *>(dst) = *reinterpret_cast<const int4_t *>(h);
-    *reinterpret_cast<int4_t *>(dst + 8) = *reinterpret_cast<const int4_t *>(h + 4);
-  }
+    for (int k = 0; k < K; ++k) {
+      const int c = (threadIdx.x + k * NTH) * 16;
+      half2_t h[8];
 #pragma unroll
-  for (int k = 0; k < KD; ++k) {
-    const int b = threadIdx.x + k * NTH;
-    float *dst = b < nwin * (kWinCols / 32) ? dsc + b : reinterpret_cast<float *>(sink);
-    *dst = dv[k];
+      for (int j = 0; j < 4; ++j) i8x4_to_f16((uint32_t)aq[tt][k][j], h[2 * j], h[2 * j + 1]);
+      // Window layout: the first 8 values of all 64 lanes' chunks, then the last 8, so that
+      // each of a lane's two 16-byte LDS reads is contiguous across the wave (no bank
+      // conflicts).  Chunk c / 16 is lane (c / 16) % 64 of window c / 1024.
+      const int base = (c / kWinCols) * kWinCols + ((c / 16) % kWave) * 8;
+      _Float16 *lo = c < nwin * kWinCols ? act + base : reinterpret_cast<_Float16 *>(sink);
+      _Float16 *hi = c < nwin * kWinCols ? act + base + kWinCols / 2 : reinterpret_cast<_Float16 *>(sink);
+      *reinterpret_cast<int4_t *>(lo) = *reinterpret_cast<const int4_t *>(h);
+      *reinterpret_cast<int4_t *>(hi) = *reinterpret_cast<const int4_t *>(h + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+      const int b = threadIdx.x + k * NTH;
+      float *dst = b < nwin * (kWinCols / 32) ? dsc + b : reinterpret_cast<float *>(sink);
+      *dst = dv[tt][k];
+    }
   }
   __syncthreads();
 
   // 4. stream.
-  float acc[RPW];
+  float acc[MT][RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+  for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[tt][r] = 0.0f;
   auto compute = [&](const int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
       if (win < wend) {
         const int col = win * kWinCols + lane * 16;
-        half2_t a[8];
-        *reinterpret_cast<int4_t *>(a) = *reinterpret_cast<const int4_t *>(act + col);
-        *reinterpret_cast<int4_t *>(a + 4) = *reinterpret_cast<const int4_t *>(act + col + 8);
-        const float sc = dsc[col / 32];
+        half2_t wh[RPW][8];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r] = fmaf(dot16(wb[u][r], a), sc, acc[r]);
+        for (int r = 0; r < RPW; ++r) decode16(wb[u][r], wh[r]);
+        // Activation row tt's 16 values and block scale from LDS; row tt + 1 is read while
+        // row tt is multiplied, so the LDS latency is not paid once per row.
+        auto read_row = [&](int tt, half2_t (&a)[8], float &sc) {
+          const _Float16 *act = reinterpret_cast<const _Float16 *>(lds + tt * row_lds);
+          const float *dsc =
+              reinterpret_cast<const float *>(lds + tt * row_lds + (size_t)nwin * kWinCols * 2);
+          const int base = win * kWinCols + lane * 8;
+          *reinterpret_cast<int4_t *>(a) = *reinterpret_cast<const int4_t *>(act + base);
+          *reinterpret_cast<int4_t *>(a + 4) =
+              *reinterpret_cast<const int4_t *>(act + base + kWinCols / 2);
+          sc = dsc[col / 32];
+        };
+        half2_t a[2][8];
+        float sc[2];
+        read_row(0, a[0], sc[0]);
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt) {
+          if (tt + 1 < MT) read_row(tt + 1, a[(tt + 1) & 1], sc[(tt + 1) & 1]);
+#pragma unroll
+          for (int r = 0; r < RPW; ++r)
+            acc[tt][r] = fmaf(dot16(wh[r], a[tt & 1]), sc[tt & 1], acc[tt][r]);
+        }
       }
     }
   };
@@ -215,26 +266,36 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
 
   if constexpr (SPLIT == 1) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float s = wave_sum(acc[r]);
-      if (lane == 0 && rok[r]) y[(int64_t)t * out_f + rbase + r] = BLK ? s : s * scale;
+    for (int tt = 0; tt < MT; ++tt) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float s = wave_sum(acc[tt][r]);
+        if (lane == 0 && rok[r] && t0 + tt < m)
+          y[(int64_t)(t0 + tt) * out_f + rbase + r] = BLK ? s : s * scale;
+      }
     }
   } else {
     // the SPLIT partial sums of a row meet in LDS and are added in part order
-    __shared__ float psum[C::WAVES * RPW];
+    __shared__ float psum[MT][C::WAVES * RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float s = wave_sum(acc[r]);
-      if (lane == 0) psum[wave * RPW + r] = s;
+    for (int tt = 0; tt < MT; ++tt) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float s = wave_sum(acc[tt][r]);
+        if (lane == 0) psum[tt][wave * RPW + r] = s;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      if (lane == 0 && part == 0 && rok[r]) {
-        float s = psum[wave * RPW + r];
+    for (int tt = 0; tt < MT; ++tt) {
 #pragma unroll
-        for (int p = 1; p < SPLIT; ++p) s += psum[(wave + p) * RPW + r];
-        y[(int64_t)t * out_f + rbase + r] = BLK ? s : s * scale;
+      for (int r = 0; r < RPW; ++r) {
+        if (lane == 0 && part == 0 && rok[r] && t0 + tt < m) {
+          float s = psum[tt][wave * RPW + r];
+#pragma unroll
+          for (int p = 1; p < SPLIT; ++p) s += psum[tt][(wave + p) * RPW + r];
+          y[(int64_t)(t0 + tt) * out_f + rbase + r] = BLK ? s : s * scale;
+        }
       }
     }
   }
@@ -247,15 +308,16 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
   auto kern = k_gemv_e4m3<BLK, C>;
   static bool attr_set = false;
   if (!attr_set) {
+    const size_t want = C::MT * act_lds_bytes(C::MAX_IN_F) + kSinkBytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(act_lds_bytes(C::MAX_IN_F) + kSinkBytes));
+                                       (int)(want < kLdsBytes ? want : kLdsBytes));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, m);
-  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), act_lds_bytes(in_f) + kSinkBytes, s, W, row_bytes, scale,
-                     grid, grid_cols, qs, d, y, in_f, out_f);
+  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, (m + C::MT - 1) / C::MT);
+  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), C::MT * act_lds_bytes(in_f) + kSinkBytes, s, W,
+                     row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f);
   return hipGetLastError();
 }
 
@@ -264,25 +326,52 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
 // per row there (long rows, few of them: splitting keeps more, shorter-lived waves in
 // flight; 6% faster at 5120 x 17408); 16 waves beyond.  All double-buffer their windows
 // (2 to 4 per batch) and fit 64 VGPRs.
-using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;      // in_f <= 8192
-using CfgMid = Cfg<8, 1, 3, 3, 2, true, 8, 2>;  // in_f <= 24576
-using CfgLarge = Cfg<16, 1, 4, 4, 4, true>;  // in_f <= 65536
-static_assert(CfgSmall::MAX_IN_F == 8192 && CfgMid::MAX_IN_F >= 24576 &&
+// Several activation rows (m > 1) share each weight pass: up to 8 rows per workgroup for
+// in_f <= 8192, 2 beyond 8192 (LDS holds one staged row per activation row).  Every shape
+// used for one in_f range splits rows the same way (SPLIT), so each activation row is
+// computed in the same order whatever m is.
+using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;                // in_f <= 8192, m = 1
+using CfgSmallB2 = Cfg<4, 1, 2, 2, 1, true, 8, 1, 2>;     //               m = 2
+using CfgSmallB4 = Cfg<8, 2, 1, 1, 1, true, 6, 1, 4>;     //               m = 3..4
+using CfgSmallB8 = Cfg<16, 2, 1, 1, 1, true, 4, 1, 8>;    //               m >= 5
+using CfgMid = Cfg<8, 1, 3, 3, 2, true, 8, 2>;            // in_f <= 24576, m = 1
+using CfgMidB2 = Cfg<8, 1, 3, 3, 2, true, 8, 2, 2>;       //                m >= 2
+using CfgLarge = Cfg<16, 1, 4, 4, 4, true>;               // in_f <= 65536
+static_assert(CfgSmall::MAX_IN_F == 8192 && CfgSmallB2::MAX_IN_F >= 8192 &&
+                  CfgSmallB4::MAX_IN_F >= 8192 && CfgSmallB8::MAX_IN_F >= 8192 &&
+                  CfgMid::MAX_IN_F >= 24576 && CfgMidB2::MAX_IN_F >= 24576 &&
                   CfgLarge::MAX_IN_F == kMaxInF, "activation coverage");
 static_assert(CfgSmall::KD * CfgSmall::THREADS * 32 >= CfgSmall::MAX_IN_F &&
+                  CfgSmallB2::KD * CfgSmallB2::THREADS * 32 >= 8192 &&
+                  CfgSmallB4::KD * CfgSmallB4::THREADS * 32 >= 8192 &&
+                  CfgSmallB8::KD * CfgSmallB8::THREADS * 32 >= 8192 &&
                   CfgMid::KD * CfgMid::THREADS * 32 >= CfgMid::MAX_IN_F &&
+                  CfgMidB2::KD * CfgMidB2::THREADS * 32 >= 24576 &&
                   CfgLarge::KD * CfgLarge::THREADS * 32 >= CfgLarge::MAX_IN_F,
               "scale coverage");
+static_assert(CfgSmallB8::MT * act_lds_bytes(8192) + kSinkBytes <= kLdsBytes &&
+                  CfgMidB2::MT * act_lds_bytes(24576) + kSinkBytes <= kLdsBytes &&
+                  act_lds_bytes(kMaxInF) + kSinkBytes <= kLdsBytes,
+              "staged rows fit the LDS of a workgroup");
+static_assert(CfgSmall::SPLIT == CfgSmallB2::SPLIT && CfgSmall::SPLIT == CfgSmallB4::SPLIT &&
+                  CfgSmall::SPLIT == CfgSmallB8::SPLIT && CfgMid::SPLIT == CfgMidB2::SPLIT,
+              "one row split per in_f range");
 
 template <bool BLK>
 hipError_t dispatch(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                     int grid_cols, const int8_t *qs, const float *d, float *y, int m, int in_f,
                     int out_f, hipStream_t s) {
-  if (in_f <= CfgSmall::MAX_IN_F)
-    return launch_cfg<BLK, CfgSmall>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
-  if (in_f <= CfgMid::MAX_IN_F)
-    return launch_cfg<BLK, CfgMid>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
-  return launch_cfg<BLK, CfgLarge>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+#define FP8GEMV_LAUNCH(CFG) \
+  launch_cfg<BLK, CFG>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s)
+  if (in_f <= 8192) {
+    if (m == 1) return FP8GEMV_LAUNCH(CfgSmall);
+    if (m == 2) return FP8GEMV_LAUNCH(CfgSmallB2);
+    if (m <= 4) return FP8GEMV_LAUNCH(CfgSmallB4);
+    return FP8GEMV_LAUNCH(CfgSmallB8);
+  }
+  if (in_f <= 24576) return m == 1 ? FP8GEMV_LAUNCH(CfgMid) : FP8GEMV_LAUNCH(CfgMidB2);
+  return FP8GEMV_LAUNCH(CfgLarge);
+#undef FP8GEMV_LAUNCH
 }
 
 }  // namespace

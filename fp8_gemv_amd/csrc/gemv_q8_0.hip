@@ -60,11 +60,14 @@ __host__ __device__ constexpr int windows_per_row(int in_f) {
 // padded with zeros to whole windows plus one group).
 // DB: double-buffered window loop -- the next U windows are loaded before the current U are
 // consumed, so a wave never waits with nothing in flight (rows of many windows).
+// MT: activation rows per workgroup.  Each weight chunk is loaded once and used for all MT
+// rows; every row gets the same exact integer sums and the same float operations as MT = 1.
 template <int WAVES_, int RPW_, int U_, int KQ_, int KD_, bool DB_ = false, int WPE_ = 8,
-          int SPLIT_ = 1>
+          int SPLIT_ = 1, int MT_ = 1>
 struct QCfg {
   static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, KQ = KQ_, KD = KD_, WPE = WPE_;
   static constexpr bool DB = DB_;
+  static constexpr int MT = MT_;
   static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
   static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
   static constexpr int THREADS = WAVES * kWave;
@@ -76,11 +79,16 @@ struct QCfg {
 // with nothing to stage, so that the staging code has no branches (a branch would let the
 // compiler sink an activation load behind the weight loads and then wait for all of them).
 constexpr size_t kSinkBytes = 48;
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one CU, the most a workgroup may use
 __host__ __device__ constexpr size_t dsc_entries(int in_f) {
   return (size_t)windows_per_row(in_f) * kWinBlocks + 8;
 }
-__host__ __device__ constexpr size_t fast_lds_bytes(int in_f) {
-  return (size_t)windows_per_row(in_f) * kWinBytes + dsc_entries(in_f) * 4 + kSinkBytes;
+// One staged activation row (16-byte multiple: 816 * nwin + 4 * (24 * nwin + 8)).
+__host__ __device__ constexpr size_t row_lds_bytes(int in_f) {
+  return (size_t)windows_per_row(in_f) * kWinBytes + dsc_entries(in_f) * 4;
+}
+__host__ __device__ constexpr size_t fast_lds_bytes(int in_f, int mt) {
+  return (size_t)mt * row_lds_bytes(in_f) + kSinkBytes;
 }
 
 // Wave-wide shift right by one lane (DPP wave_shr:1); lane 0 receives 0.
@@ -93,8 +101,8 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
                       const int8_t *__restrict__ qs, const float *__restrict__ d,
-                      float *__restrict__ y, int in_f, int out_f) {
-  constexpr int RPW = C::RPW, U = C::U, KQ = C::KQ, KD = C::KD, NTH = C::THREADS;
+                      float *__restrict__ y, int m, int in_f, int out_f) {
+  constexpr int RPW = C::RPW, U = C::U, KQ = C::KQ, KD = C::KD, NTH = C::THREADS, MT = C::MT;
   constexpr int SPLIT = C::SPLIT;
   static_assert(C::WAVES % SPLIT == 0, "whole row groups per workgroup");
   extern __shared__ __align__(16) unsigned char lds[];
@@ -102,28 +110,34 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   const int row_used = nb * kBlkBytes;  // used bytes of a row (a multiple of 16)
   const int nwin = windows_per_row(in_f);
   const int ndsc = nwin * kWinBlocks + 8;
-  uint8_t *shaped = lds;                                                   // nwin * 816 bytes
-  float *dsc = reinterpret_cast<float *>(lds + (size_t)nwin * kWinBytes);  // ndsc entries
-  const int t = blockIdx.y;
+  const int row_lds = (int)row_lds_bytes(in_f);
+  // activation row tt: shaped bytes at lds + tt * row_lds (nwin * 816), then ndsc scales
+  const int t0 = blockIdx.y * MT;  // first activation row of this workgroup
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
   const int rbase = (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
   const int part = wave % SPLIT;
   const int wbeg = part * nwin / SPLIT, wend = (part + 1) * nwin / SPLIT;  // this wave's windows
-  const rsrc_t qrs = buf_rsrc(qs + (int64_t)t * in_f, (uint32_t)in_f);
-  const rsrc_t drs = buf_rsrc(d + (int64_t)t * nb, (uint32_t)nb * 4);
 
-  // 1. this thread's activation blocks and scales (oldest loads; zeros past the row).
-  int4_t aq[KQ][2];
-  float dv[KD];
+  // 1. this thread's activation blocks and scales of the MT rows (oldest loads; zeros past
+  // the row and for rows past m).
+  int4_t aq[MT][KQ][2];
+  float dv[MT][KD];
 #pragma unroll
-  for (int k = 0; k < KQ; ++k) {
-    const uint32_t off = (uint32_t)(threadIdx.x + k * NTH) * 32;
-    aq[k][0] = buf_load16(qrs, off);
-    aq[k][1] = buf_load16(qrs, off + 16);
+  for (int tt = 0; tt < MT; ++tt) {
+    const bool tok = t0 + tt < m;
+    const rsrc_t qrs = buf_rsrc(qs + (int64_t)(tok ? t0 + tt : 0) * in_f, tok ? (uint32_t)in_f : 0u);
+    const rsrc_t drs = buf_rsrc(d + (int64_t)(tok ? t0 + tt : 0) * nb, tok ? (uint32_t)nb * 4 : 0u);
+#pragma unroll
+    for (int k = 0; k < KQ; ++k) {
+      const uint32_t off = (uint32_t)(threadIdx.x + k * NTH) * 32;
+      aq[tt][k][0] = buf_load16(qrs, off);
+      aq[tt][k][1] = buf_load16(qrs, off + 16);
+    }
+#pragma unroll
+    for (int k = 0; k < KD; ++k)
+      dv[tt][k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
   }
-#pragma unroll
-  for (int k = 0; k < KD; ++k) dv[k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
 
   // 2. the first batch of weight loads: one resource per row over the used bytes of this
   // wave's windows (none for a row past out_f), so chunks past them read as zeros.  Lanes
@@ -150,9 +164,11 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   // 3. stage the activation in the shape of a Q8_0 row -- per block two zero bytes where the
   // weight row has its fp16 scale, then the 32 qs -- with zeros to the end of the last
   // window, and d_a with zeros past nb.
-  {
-    uint16_t *sh16 = reinterpret_cast<uint16_t *>(shaped);
-    unsigned char *sink = lds + fast_lds_bytes(in_f) - kSinkBytes;
+  unsigned char *sink = lds + MT * row_lds;
+#pragma unroll
+  for (int tt = 0; tt < MT; ++tt) {
+    uint16_t *sh16 = reinterpret_cast<uint16_t *>(lds + tt * row_lds);
+    float *dsc = reinterpret_cast<float *>(lds + tt * row_lds + nwin * kWinBytes);
 #pragma unroll
     for (int k = 0; k < KQ; ++k) {
       const int b = threadIdx.x + k * NTH;
@@ -163,8 +179,8 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          dst[1 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] & 0xFFFFu);
-          dst[2 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[k][h][j] >> 16);
+          dst[1 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[tt][k][h][j] & 0xFFFFu);
+          dst[2 + 8 * h + 2 * j] = (uint16_t)((uint32_t)aq[tt][k][h][j] >> 16);
         }
       }
     }
@@ -173,7 +189,7 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
     for (int k = 0; k < KD; ++k) {
       const int b = threadIdx.x + k * NTH;
       float *dst = b < ndsc ? dsc + b : reinterpret_cast<float *>(sink);
-      *dst = dv[k];
+      *dst = dv[tt][k];
     }
   }
 
@@ -202,34 +218,72 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   const int lds_lane = lane < kWinLanes ? lane * 16 : 0;  // lanes 51..63 multiply zero weights
   __syncthreads();
 
-  float acc[RPW];
+  float acc[MT][RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+  for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[tt][r] = 0.0f;
 
   auto compute = [&](const int4_t (&wb)[U][RPW], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
       if (win >= wend) break;
-      const int4_t a = *reinterpret_cast<const int4_t *>(shaped + win * kWinBytes + lds_lane);
-      const float da_h = dsc[win * kWinBlocks + dsc_lane];
+      // Per weight row: the scale bytes of the chunk (fp16 -> f32) and, for MT > 1, the
+      // dwords of b0 and of b0 + 1 as two masked copies of the chunk, shared by all rows (the
+      // integer sums are exact, so they equal the MT = 1 prefix sums).
+      float hw[RPW];
+      int4_t wlo[RPW], whi[RPW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const int4_t w = wb[u][r];
         const uint32_t hbits = __builtin_amdgcn_perm((uint32_t)w[1], (uint32_t)w[0], sel_lo) |
                                __builtin_amdgcn_perm((uint32_t)w[3], (uint32_t)w[2], sel_hi);
-        const float H = (float)__builtin_bit_cast(_Float16, (uint16_t)hbits) * da_h;
-        const float h1 = wave_shr1(H);   // scale of chunk c - 1
-        const float h2 = wave_shr1(h1);  // scale of chunk c - 2
-        const int t1 = __builtin_amdgcn_sdot4(w[0], a[0], 0, false);
-        const int t2 = __builtin_amdgcn_sdot4(w[1], a[1], t1, false);
-        const int t3 = __builtin_amdgcn_sdot4(w[2], a[2], t2, false);
-        const int t4 = __builtin_amdgcn_sdot4(w[3], a[3], t3, false);
-        const int s_lo = lo_4 ? t4 : (lo_ge3 ? t3 : (lo_ge2 ? t2 : t1));
-        const int s_hi = t4 - s_lo;
-        const float S0 = d0 ? H : (d1 ? h1 : h2);
-        acc[r] = fmaf((float)s_lo, S0, acc[r]);
-        acc[r] = fmaf((float)s_hi, H, acc[r]);
+        hw[r] = (float)__builtin_bit_cast(_Float16, (uint16_t)hbits);
+        wlo[r] = int4_t{w[0], lo_ge2 ? w[1] : 0, lo_ge3 ? w[2] : 0, lo_4 ? w[3] : 0};
+        whi[r] = int4_t{0, lo_ge2 ? 0 : w[1], lo_ge3 ? 0 : w[2], lo_4 ? 0 : w[3]};
+      }
+      // Activation row tt's chunk and scale from LDS; row tt + 1 is read while row tt is
+      // multiplied, so the LDS latency is not paid once per row.
+      auto read_row = [&](int tt, int4_t &a, float &da) {
+        const unsigned char *arow = lds + tt * row_lds;
+        a = *reinterpret_cast<const int4_t *>(arow + win * kWinBytes + lds_lane);
+        da = reinterpret_cast<const float *>(arow + nwin * kWinBytes)[win * kWinBlocks + dsc_lane];
+      };
+      int4_t abuf[2];
+      float dbuf[2];
+      read_row(0, abuf[0], dbuf[0]);
+#pragma unroll
+      for (int tt = 0; tt < MT; ++tt) {
+        if (tt + 1 < MT) read_row(tt + 1, abuf[(tt + 1) & 1], dbuf[(tt + 1) & 1]);
+        const int4_t a = abuf[tt & 1];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const float H = hw[r] * dbuf[tt & 1];
+          const float h1 = wave_shr1(H);   // scale of chunk c - 1
+          const float h2 = wave_shr1(h1);  // scale of chunk c - 2
+          int s_lo, s_hi;
+          if constexpr (MT == 1) {
+            const int4_t w = wb[u][r];
+            const int t1 = __builtin_amdgcn_sdot4(w[0], a[0], 0, false);
+            const int t2 = __builtin_amdgcn_sdot4(w[1], a[1], t1, false);
+            const int t3 = __builtin_amdgcn_sdot4(w[2], a[2], t2, false);
+            const int t4 = __builtin_amdgcn_sdot4(w[3], a[3], t3, false);
+            s_lo = lo_4 ? t4 : (lo_ge3 ? t3 : (lo_ge2 ? t2 : t1));
+            s_hi = t4 - s_lo;
+          } else {
+            s_lo = __builtin_amdgcn_sdot4(wlo[r][0], a[0], 0, false);
+            s_lo = __builtin_amdgcn_sdot4(wlo[r][1], a[1], s_lo, false);
+            s_lo = __builtin_amdgcn_sdot4(wlo[r][2], a[2], s_lo, false);
+            s_lo = __builtin_amdgcn_sdot4(wlo[r][3], a[3], s_lo, false);
+            s_hi = __builtin_amdgcn_sdot4(whi[r][1], a[1], 0, false);
+            s_hi = __builtin_amdgcn_sdot4(whi[r][2], a[2], s_hi, false);
+            s_hi = __builtin_amdgcn_sdot4(whi[r][3], a[3], s_hi, false);
+          }
+          const float S0 = d0 ? H : (d1 ? h1 : h2);
+          acc[tt][r] = fmaf((float)s_lo, S0, acc[tt][r]);
+          acc[tt][r] = fmaf((float)s_hi, H, acc[tt][r]);
+        }
       }
     }
   };
@@ -260,26 +314,35 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
 
   if constexpr (SPLIT == 1) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float s = wave_sum(acc[r]);
-      if (lane == 0 && rok[r]) y[(int64_t)t * out_f + rbase + r] = s;
+    for (int tt = 0; tt < MT; ++tt) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float s = wave_sum(acc[tt][r]);
+        if (lane == 0 && rok[r] && t0 + tt < m) y[(int64_t)(t0 + tt) * out_f + rbase + r] = s;
+      }
     }
   } else {
     // the SPLIT partial sums of a row meet in LDS and are added in part order
-    __shared__ float psum[C::WAVES * RPW];
+    __shared__ float psum[MT][C::WAVES * RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float s = wave_sum(acc[r]);
-      if (lane == 0) psum[wave * RPW + r] = s;
+    for (int tt = 0; tt < MT; ++tt) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float s = wave_sum(acc[tt][r]);
+        if (lane == 0) psum[tt][wave * RPW + r] = s;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      if (lane == 0 && part == 0 && rok[r]) {
-        float s = psum[wave * RPW + r];
+    for (int tt = 0; tt < MT; ++tt) {
 #pragma unroll
-        for (int p = 1; p < SPLIT; ++p) s += psum[(wave + p) * RPW + r];
-        y[(int64_t)t * out_f + rbase + r] = s;
+      for (int r = 0; r < RPW; ++r) {
+        if (lane == 0 && part == 0 && rok[r] && t0 + tt < m) {
+          float s = psum[tt][wave * RPW + r];
+#pragma unroll
+          for (int p = 1; p < SPLIT; ++p) s += psum[tt][(wave + p) * RPW + r];
+          y[(int64_t)(t0 + tt) * out_f + rbase + r] = s;
+        }
       }
     }
   }
@@ -322,15 +385,16 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
   auto kern = k_gemv_q8_0_fast<C>;
   static bool attr_set = false;
   if (!attr_set) {
+    const size_t want = fast_lds_bytes(C::MAX_IN_F, C::MT);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)fast_lds_bytes(C::MAX_IN_F));
+                                       (int)(want < kLdsBytes ? want : kLdsBytes));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, m);
-  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes(in_f), s, W, row_bytes, qs, d,
-                     y, in_f, out_f);
+  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, (m + C::MT - 1) / C::MT);
+  hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes(in_f, C::MT), s, W, row_bytes, qs,
+                     d, y, m, in_f, out_f);
   return hipGetLastError();
 }
 
@@ -339,15 +403,37 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
 // two groups).  In the middle range two waves share each row (4 rows per workgroup): rows of
 // 17408 columns are 23 windows, and with one wave per row a 5120-row matrix would keep only
 // 20 long-lived waves per CU, unevenly spread.
-using QSmall = QCfg<4, 1, 3, 1, 2, true>;         // in_f <= 8192
-using QMid = QCfg<8, 1, 4, 2, 3, true, 8, 2>;     // in_f <= 32768
-using QLarge = QCfg<16, 1, 4, 2, 3, true>;  // in_f <= 65536
-static_assert(QSmall::MAX_IN_F >= 8192 && QMid::MAX_IN_F >= 24576 && QLarge::MAX_IN_F == kMaxInF,
+// Several activation rows (m > 1) share each weight pass: up to 8 rows per workgroup for
+// in_f <= 8192, 2 beyond 8192 (LDS holds one staged row per activation row).  Every shape
+// used for one in_f range splits rows the same way (SPLIT), so each activation row is
+// computed in the same order whatever m is.
+using QSmall = QCfg<4, 1, 3, 1, 2, true>;                 // in_f <= 8192, m = 1
+using QSmallB2 = QCfg<4, 1, 3, 1, 2, true, 8, 1, 2>;      //               m = 2
+using QSmallB4 = QCfg<8, 1, 2, 1, 2, true, 6, 1, 4>;      //               m = 3..4
+using QSmallB8 = QCfg<8, 2, 1, 1, 3, true, 4, 1, 8>;      //               m >= 5
+using QMid = QCfg<8, 1, 4, 2, 3, true, 8, 2>;             // in_f <= 24576, m = 1
+using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 2, 2>;        //                m >= 2
+using QLarge = QCfg<16, 1, 4, 2, 3, true>;                // in_f <= 65536
+static_assert(QSmall::MAX_IN_F >= 8192 && QSmallB2::MAX_IN_F >= 8192 &&
+                  QSmallB4::MAX_IN_F >= 8192 && QSmallB8::MAX_IN_F >= 8192 &&
+                  QMid::MAX_IN_F >= 24576 && QMidB2::MAX_IN_F >= 24576 &&
+                  QLarge::MAX_IN_F == kMaxInF,
               "activation coverage of the in_f ranges dispatched to each shape");
 static_assert(QSmall::KD * QSmall::THREADS >= (int)dsc_entries(QSmall::MAX_IN_F) &&
+                  QSmallB2::KD * QSmallB2::THREADS >= (int)dsc_entries(8192) &&
+                  QSmallB4::KD * QSmallB4::THREADS >= (int)dsc_entries(8192) &&
+                  QSmallB8::KD * QSmallB8::THREADS >= (int)dsc_entries(8192) &&
                   QMid::KD * QMid::THREADS >= (int)dsc_entries(QMid::MAX_IN_F) &&
+                  QMidB2::KD * QMidB2::THREADS >= (int)dsc_entries(24576) &&
                   QLarge::KD * QLarge::THREADS >= (int)dsc_entries(QLarge::MAX_IN_F),
               "scale coverage");
+static_assert(fast_lds_bytes(8192, QSmallB8::MT) <= kLdsBytes &&
+                  fast_lds_bytes(24576, QMidB2::MT) <= kLdsBytes &&
+                  fast_lds_bytes(kMaxInF, 1) <= kLdsBytes,
+              "staged rows fit the LDS of a workgroup");
+static_assert(QSmall::SPLIT == QSmallB2::SPLIT && QSmall::SPLIT == QSmallB4::SPLIT &&
+                  QSmall::SPLIT == QSmallB8::SPLIT && QMid::SPLIT == QMidB2::SPLIT,
+              "one row split per in_f range");
 
 }  // namespace
 
@@ -356,8 +442,16 @@ hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *q
   const bool fast = (in_f % 256 == 0) && (row_bytes % 16 == 0) &&
                     ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
   if (fast) {
-    if (in_f <= 8192) return launch_fast<QSmall>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
-    if (in_f <= 24576) return launch_fast<QMid>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+    if (in_f <= 8192) {
+      if (m == 1) return launch_fast<QSmall>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+      if (m == 2) return launch_fast<QSmallB2>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+      if (m <= 4) return launch_fast<QSmallB4>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+      return launch_fast<QSmallB8>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+    }
+    if (in_f <= 24576) {
+      if (m == 1) return launch_fast<QMid>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+      return launch_fast<QMidB2>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+    }
     return launch_fast<QLarge>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
   }
   const dim3 g((out_f + kWaves - 1) / kWaves, m);

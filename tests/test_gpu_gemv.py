@@ -89,7 +89,7 @@ SMALL = [(1, 32), (7, 96), (130, 160), (131, 288), (257, 1056), (300, 2080), (64
          (129, 4352), (33, 1280), (250, 2048), (37, 8704), (5, 8224), (131, 9600), (9, 24576)]
 
 
-@pytest.mark.parametrize("m", [1, 3])
+@pytest.mark.parametrize("m", [1, 3, 5])
 @pytest.mark.parametrize("out_f,in_f", SMALL)
 @pytest.mark.parametrize("kind", KINDS)
 def test_gemv_small_shapes_match_oracle(fg, kind, out_f, in_f, m):
@@ -118,11 +118,13 @@ def test_gemv_full_shapes_sampled_rows(fg, kind, out_f, in_f):
         _assert_close(y, yo, A, rows)
 
 
+# m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
+# m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.
 @pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("kind", KINDS)
 def test_gemv_m_rows_bit_identical_to_m1(fg, kind, out_f, in_f):
-    c = Case(kind, out_f, in_f, 8)
-    for m in (1, 2, 4, 8):
+    c = Case(kind, out_f, in_f, 11)
+    for m in (1, 2, 3, 4, 5, 8, 11):
         case(f"{kind} m={m} out_f={out_f} in_f={in_f}")
         y = c.gpu(fg, qs=to_dev(c.qs[:m]), d=to_dev(c.d[:m]), m=m)
         for t in range(m):
