@@ -38,6 +38,14 @@ SHAPES = [(5120, 5120), (17408, 5120), (5120, 17408)]  # [out_f, in_f]
 ARMS = ["e4m3", "blk128", "q8_0"]
 SCALE = 2.0 ** -4
 EPS = 1e-6
+# The projection shape sheets of the bench page ([out_f, in_f], label): the 27B sheet carries
+# the verdict, the 1.7B sheet is reported alongside.
+SHEETS = {
+    "27b": [(12288, 5120, "q_proj"), (1024, 5120, "k/v_proj"), (5120, 6144, "o_proj"),
+            (17408, 5120, "gate/up_proj"), (5120, 17408, "down_proj"), (5120, 5120, "square-ref")],
+    "1p7b": [(2048, 2048, "q_proj"), (1024, 2048, "k/v_proj"), (2048, 2048, "o_proj"),
+             (6144, 2048, "gate/up_proj"), (2048, 6144, "down_proj")],
+}
 M_ROWS = (1, 2, 4, 8)   # small-batch activation rows, timed at SHAPE_M
 MAX_M = max(M_ROWS)
 SHAPE_M = (17408, 5120)
@@ -280,6 +288,8 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run 4 device-to-device copies of this many MiB (a plain copy "
                          "kernel of known size that calibrates the HBM byte counters)")
+    ap.add_argument("--no-sheets", action="store_true",
+                    help="skip the 27B / 1.7B projection shape sheets")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print a markdown summary of a rocprofv3 kernel trace and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -434,6 +444,51 @@ def main() -> int:
                     "alg_bytes": algorithmic_bytes(a, out_f, in_f, m)}
                 log(f"{a:7s} {out_f}x{in_f} m={m}: {us:8.2f} us  {us / m:7.2f} us/row")
 
+    # Projection shape sheets (gemv_e4m3_bench.rs, main: the 27B and 1.7B sheets, the three
+    # arms per shape on their own rotated copies, ratio = t_q8_0 / t_e4m3, ratio_blk =
+    # t_q8_0 / t_blk, blk/e4m3 = t_e4m3 / t_blk, and geometric means over each sheet).
+    sheets = {}
+    if not (args.kernels_only or args.no_sheets):
+        x1 = {}
+        for name, sheet in SHEETS.items():
+            rows_out, lns, lns_blk = [], [], []
+            for out_f, in_f, label in sheet:
+                if in_f not in x1:
+                    xs = torch.from_numpy(synth.x_rows(in_f, 1)).to(dev)
+                    ws = torch.from_numpy(synth.gain(in_f)).to(dev)
+                    qs1 = torch.empty(in_f, dtype=torch.int8, device=dev)
+                    d1 = torch.empty(in_f // 32, device=dev)
+                    fg.rmsnorm_q8_1(xs, ws, None, qs1, d1, in_f, 1, EPS)
+                    x1[in_f] = (qs1, d1)
+                qs1, d1 = x1[in_f]
+                t = {}
+                for a in ARMS:
+                    obj = Arm(fg, torch, a, out_f, in_f, dev)
+                    n = max(args.kernel_iters, obj.copies)
+                    g = capture(lambda: [obj.launch(qs1, d1) for _ in range(n)])
+                    g.replay()
+                    t[a] = timed(g.replay, n) * 1e3
+                    del g, obj
+                row = {"shape": label, "out_f": out_f, "in_f": in_f,
+                       "e4m3_us": round(t["e4m3"], 3), "blk_us": round(t["blk128"], 3),
+                       "q8_0_us": round(t["q8_0"], 3),
+                       "ratio": round(t["q8_0"] / t["e4m3"], 4),
+                       "ratio_blk": round(t["q8_0"] / t["blk128"], 4),
+                       "blk_over_e4m3": round(t["e4m3"] / t["blk128"], 4),
+                       "blk_GBs": round(out_f * in_f / t["blk128"] / 1e3, 1)}
+                rows_out.append(row)
+                lns.append(math.log(row["ratio"]))
+                lns_blk.append(math.log(row["ratio_blk"]))
+                log(f"sheet {name} {label:12s} {in_f}->{out_f}: e4m3 {t['e4m3']:.2f} blk "
+                    f"{t['blk128']:.2f} q8_0 {t['q8_0']:.2f} us")
+            geo, geo_blk = math.exp(sum(lns) / len(lns)), math.exp(sum(lns_blk) / len(lns_blk))
+            sheets[name] = {"rows": rows_out, "geomean_ratio": round(geo, 4),
+                            "geomean_ratio_blk": round(geo_blk, 4),
+                            "delta_pp": round(100 * (geo - 1), 2),
+                            "delta_pp_blk": round(100 * (geo_blk - 1), 2),
+                            "byte_ratio": 34 / 32}
+            torch.cuda.empty_cache()
+
     # Achievable read ceiling: the library's streaming-read measurement kernel over the same
     # rotated e4m3 copies (same bytes, same load pattern, no arithmetic).
     ceiling = {}
@@ -505,7 +560,8 @@ def main() -> int:
                    "eps": EPS, "e4m3_scale": SCALE},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
-        "gemv": detail, "read_ceiling": ceiling, "m_rows": m_rows, "producer_us": prod_us,
+        "gemv": detail, "read_ceiling": ceiling, "m_rows": m_rows, "sheets": sheets,
+        "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -15,6 +15,8 @@ What it computes (docs.rs pages of memra-engine 0.125.0):
   in f32 -- see ``oracle.c``.
 * The three GEMVs of the bench page (src/bin/gemv_e4m3_bench.rs, module doc THE COMPARISON
   and THE BLOCK-128 ARM), f64 terms and sums -- see ``oracle.c``.
+* The load-time e4m3 -> Q8_0 requantisation the same page names as its ship path (QUESTION),
+  in f32 with an fp16 block scale -- see ``oracle.c`` for the reading it takes.
 
 Readings where the pages are silent are listed in the repository's design notes; the ones that
 decide a value are restated next to the function that takes them.
@@ -65,6 +67,10 @@ def _load():
         lib.oracle_gemv_e4m3_blk128.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, i32, i32,
                                                 i32, vp, vp]
         lib.oracle_gemv_e4m3_blk128.restype = i32
+        lib.oracle_f32_to_fp16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_fp16.restype = ctypes.c_uint16
+        lib.oracle_requant_q8_0.argtypes = [vp, i64, f32, vp, i32, vp, i64, i32, i32, i32, i32]
+        lib.oracle_requant_q8_0.restype = i32
         _lib = lib
     return _lib
 
@@ -202,3 +208,36 @@ def gemv_e4m3_blk128(W, row_bytes, grid, qs, d, in_f, out_f, rows=None):
     if rc != 0:
         raise ValueError(f"oracle_gemv_e4m3_blk128 refused its input ({rc})")
     return y, A
+
+
+# ---------------------------------------------------------------------- requantiser
+
+def f32_to_fp16(x: float) -> int:
+    """binary16 bit pattern of an f32, round to nearest even."""
+    return int(_load().oracle_f32_to_fp16(float(np.float32(x))))
+
+
+def requant_q8_0(W, row_bytes, in_f, out_f, scale=None, grid=None, rows=None, q_row_bytes=None):
+    """e4m3 rows -> ggml Q8_0 rows (per-tensor ``scale`` or block-128 ``grid``).
+
+    Returns uint8 [out_f, q_row_bytes] (q_row_bytes defaults to in_f / 32 * 34); rows outside
+    ``rows`` and bytes past each row's blocks are zero."""
+    W = _c(W, np.uint8)
+    assert (scale is None) != (grid is None)
+    nb = in_f // 32
+    qrb = nb * 34 if q_row_bytes is None else int(q_row_bytes)
+    assert W.size >= out_f * row_bytes
+    out = np.zeros((out_f, qrb), dtype=np.uint8)
+    r0, r1 = _rows(rows, out_f)
+    if grid is not None:
+        grid = _c(grid, np.float32)
+        grid_cols = (in_f + 127) // 128
+        assert grid.size == ((out_f + 127) // 128) * grid_cols
+        rc = _load().oracle_requant_q8_0(W.ctypes.data, row_bytes, 0.0, grid.ctypes.data,
+                                         grid_cols, out.ctypes.data, qrb, in_f, out_f, r0, r1)
+    else:
+        rc = _load().oracle_requant_q8_0(W.ctypes.data, row_bytes, float(scale), None, 0,
+                                         out.ctypes.data, qrb, in_f, out_f, r0, r1)
+    if rc != 0:
+        raise ValueError(f"oracle_requant_q8_0 refused its input ({rc})")
+    return out

@@ -192,3 +192,84 @@ int oracle_gemv_e4m3_blk128(const uint8_t *W, int64_t row_bytes, const float *gr
     }
     return 0;
 }
+
+/* ------------------------------------------------------------ requantiser ---- */
+
+/* IEEE binary16 bit pattern of a finite f32, rounded to nearest with ties to even; results
+ * below 2^-14 are subnormal, magnitudes from 65520 up round to infinity; NaN stays NaN.
+ * Written from the binary16 definition: |f| = n * 2^(e-10) with 1024 <= n < 2048 (normal) or
+ * n * 2^-24 with n < 1024 (subnormal); n is rounded, and a carry to 2048 moves to the next
+ * exponent. */
+static double round_half_even(double x) { /* x >= 0, exact in double */
+    double r = floor(x), diff = x - r;
+    if (diff > 0.5) return r + 1.0;
+    if (diff < 0.5) return r;
+    return fmod(r, 2.0) == 0.0 ? r : r + 1.0;
+}
+
+uint16_t oracle_f32_to_fp16(float f) {
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    double a = fabs((double)f);
+    if (isnan(f)) return sign | 0x7E00;
+    if (a >= 65520.0) return sign | 0x7C00;
+    if (a < ldexp(1.0, -14)) {
+        double n = round_half_even(ldexp(a, 24)); /* 0 .. 1024; 1024 is the least normal */
+        return sign | (uint16_t)n;
+    }
+    int ex;
+    frexp(a, &ex); /* a = fr * 2^ex, 0.5 <= fr < 1, so 2^(ex-1) <= a < 2^ex */
+    int e = ex - 1;
+    double n = round_half_even(ldexp(a, 10 - e)); /* 1024 .. 2048 */
+    if (n == 2048.0) {
+        n = 1024.0;
+        e += 1;
+    }
+    return sign | (uint16_t)((e + 15) << 10) | (uint16_t)(n - 1024.0);
+}
+
+/*
+ * Load-time requantisation of an e4m3 weight plane into ggml Q8_0 rows (the bench page's ship
+ * path, QUESTION: FP8 checkpoints are dequantised to a Q8_0 slab at load, 34 bytes per 32
+ * weights).  The page gives no formula; the plainest reading, taken here, is the same per-block
+ * rule as the q8_1 quantiser with the scale stored as fp16:
+ *   v_i  = e4m3(W[r, 32b+i]) * S          f32 multiply; S = scale, or grid[r/128, b/4] when a
+ *                                         block-128 grid is given (THE BLOCK-128 ARM)
+ *   amax = max |v_i|,  d = amax / 127     f32
+ *   q_i  = round(v_i / d), halves away from zero (0 when d == 0)
+ *   block bytes: fp16(d) little-endian, then the 32 int8 q_i.
+ * Rows r0 <= r < r1 are written at Wq + r * q_row_bytes.
+ * Returns 0, -1 for an e4m3 NaN code or a non-finite scale (refused input), -2 on bad shapes.
+ */
+int oracle_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
+                        int grid_cols, uint8_t *Wq, int64_t q_row_bytes, int in_f, int out_f,
+                        int r0, int r1) {
+    if (in_f <= 0 || in_f % 32 != 0 || out_f < 1 || r0 < 0 || r1 > out_f || r0 > r1) return -2;
+    int nb = in_f / 32;
+    if (row_bytes < in_f || q_row_bytes < (int64_t)nb * 34) return -2;
+    if (grid && grid_cols != (in_f + 127) / 128) return -2;
+    for (int r = r0; r < r1; ++r) {
+        const uint8_t *row = W + (int64_t)r * row_bytes;
+        uint8_t *out = Wq + (int64_t)r * q_row_bytes;
+        for (int b = 0; b < nb; ++b) {
+            float S = grid ? grid[(int64_t)(r / 128) * grid_cols + (32 * b) / 128] : scale;
+            if (!isfinite(S)) return -1;
+            float v[32], amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                double e = oracle_e4m3_value(row[32 * b + i]);
+                if (isnan(e)) return -1;
+                v[i] = (float)e * S;
+                float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+            float db = amax / 127.0f;
+            uint16_t h = oracle_f32_to_fp16(db);
+            out[34 * b] = (uint8_t)(h & 0xFF);
+            out[34 * b + 1] = (uint8_t)(h >> 8);
+            for (int i = 0; i < 32; ++i) {
+                int8_t q = (db != 0.0f) ? (int8_t)roundf(v[i] / db) : 0;
+                out[34 * b + 2 + i] = (uint8_t)q;
+            }
+        }
+    }
+    return 0;
+}

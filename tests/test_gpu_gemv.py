@@ -118,6 +118,24 @@ def test_gemv_full_shapes_sampled_rows(fg, kind, out_f, in_f):
         _assert_close(y, yo, A, rows)
 
 
+# The projection shapes of the 27B and 1.7B sheets not covered above ([out_f, in_f]).
+SHEET = [(12288, 5120), (1024, 5120), (5120, 6144), (2048, 2048), (1024, 2048), (6144, 2048),
+         (2048, 6144)]
+
+
+@pytest.mark.parametrize("out_f,in_f", SHEET)
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_sheet_shapes_sampled_rows(fg, kind, out_f, in_f):
+    case(f"{kind} sheet out_f={out_f} in_f={in_f}")
+    c = Case(kind, out_f, in_f, 1)
+    y = c.gpu(fg)
+    assert np.all(np.isfinite(y))
+    for r0 in (0, out_f // 2 - 37, out_f - 64):
+        rows = (r0, r0 + 64)
+        yo, A = c.oracle(rows)
+        _assert_close(y, yo, A, rows)
+
+
 # m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
 # m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.
 @pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])

@@ -322,3 +322,156 @@ def test_gemv_refuses_nan_codes():
     Wq[0, 1] = 0x7C  # f16 +inf
     with pytest.raises(ValueError):
         oracle.gemv_q8_0(Wq, 34, qs[:, :32], d[:, :1], 32, 1)
+
+
+# --------------------------------------------------------------------- requantiser
+# e4m3 -> Q8_0 at load (gemv_e4m3_bench.rs, QUESTION: the ship path dequantises FP8 checkpoints
+# to a Q8_0 slab).  The page gives no formula; the oracle takes the q8_1 block rule with an fp16
+# scale.  Pinned by hand-worked blocks, numpy's binary16 rounding, exact rationals and bounds.
+
+def _read_requant_blocks():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "q8_0_requant_blocks.txt")
+    blocks, cur = [], None
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        key, *rest = line.split()
+        if key == "block":
+            cur = {"name": rest[0], "S": float.fromhex(rest[1]) if "0x" in rest[1] else float(rest[1])}
+            blocks.append(cur)
+        elif key == "codes":
+            cur["codes"] = [int(t, 16) for t in rest]
+        elif key == "scale":
+            cur["scale"] = int(rest[0], 16)
+        elif key == "q":
+            cur["q"] = [int(t) for t in rest]
+    return blocks
+
+
+def test_requant_golden_blocks():
+    blocks = _read_requant_blocks()
+    assert len(blocks) >= 5
+    for blk in blocks:
+        W = np.array([blk["codes"]], dtype=np.uint8)
+        out = oracle.requant_q8_0(W, 32, 32, 1, scale=blk["S"])[0]
+        assert int(out[0]) | (int(out[1]) << 8) == blk["scale"], blk["name"]
+        assert out[2:].view(np.int8).tolist() == blk["q"], blk["name"]
+
+
+def test_f32_to_fp16_against_numpy():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    edge = np.array([0.0, -0.0, 65504.0, 65519.996, 65520.0, 1e9, 2.0 ** -14, 2.0 ** -24,
+                     2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -14 - 2.0 ** -25, 1.0 + 2.0 ** -11,
+                     1.0 + 3 * 2.0 ** -11, 448 / 127, -3.25e-6], dtype=np.float32)
+    for v in np.concatenate([vals[:20000], edge]):
+        want = int(np.array([v], dtype=np.float32).astype(np.float16).view(np.uint16)[0])
+        assert oracle.f32_to_fp16(float(v)) == want, repr(v)
+
+
+def _exact_block_checks(codes, S, out_block):
+    """Stored scale = binary16 nearest the exact amax / 127 (up to f32 double rounding);
+    q = rha(v * 127 / amax) unless that ratio sits within 2^-20 of a tie."""
+    v = [Fraction(oracle.e4m3_value(c)) * Fraction(S) for c in codes]
+    amax = max(abs(x) for x in v)
+    h = int(out_block[0]) | (int(out_block[1]) << 8)
+    q = out_block[2:].view(np.int8).tolist()
+    if amax == 0:
+        assert h == 0 and q == [0] * 32
+        return
+    d = amax / 127
+    got = Fraction(oracle.fp16_value(h))
+    e = math.floor(math.log2(d)) if d >= Fraction(1, 2 ** 14) else -14
+    spacing = Fraction(2) ** (e - 10)
+    assert abs(got - d) <= spacing / 2 * (1 + Fraction(1, 2 ** 12)), (h, float(d))
+    for x, qi in zip(v, q):
+        r = x / d
+        a = abs(r)
+        frac = a - math.floor(a)
+        want = (math.floor(a) + (1 if frac >= Fraction(1, 2) else 0)) * (1 if r >= 0 else -1)
+        if abs(frac - Fraction(1, 2)) < Fraction(1, 2 ** 20):
+            assert abs(qi - want) <= 1
+        else:
+            assert qi == want, (float(r), qi)
+    # the largest magnitude maps to +-127 with its sign
+    i = max(range(32), key=lambda k: abs(v[k]))
+    assert q[i] == (127 if v[i] > 0 else -127)
+
+
+def test_requant_exact_rational_per_tensor():
+    out_f, in_f = 6, 256
+    W = synth.e4m3_weights(out_f, in_f)
+    for S in (1.0, 2.0 ** -4, 0.3):
+        Q = oracle.requant_q8_0(W, in_f, in_f, out_f, scale=S)
+        for r in range(out_f):
+            for b in range(in_f // 32):
+                codes = W[r, 32 * b:32 * b + 32].tolist()
+                Sf = float(np.float32(S))
+                if S == 0.3:
+                    # v = fl32(e4m3 * S) is not exact here; check against the rounded products
+                    v32 = [float(np.float32(oracle.e4m3_value(c)) * np.float32(S)) for c in codes]
+                    amax = max(abs(x) for x in v32)
+                    h = int(Q[r, 34 * b]) | (int(Q[r, 34 * b + 1]) << 8)
+                    assert abs(oracle.fp16_value(h) - amax / 127) <= amax / 127 * 2.0 ** -10
+                    continue
+                _exact_block_checks(codes, Sf, Q[r, 34 * b:34 * b + 34])
+
+
+def test_requant_blk128_takes_the_tile_scale():
+    out_f, in_f = 130, 384  # two row tiles, three column tiles
+    W = synth.e4m3_weights(out_f, in_f)
+    grid = synth.blk128_grid(out_f, in_f)
+    Q = oracle.requant_q8_0(W, in_f, in_f, out_f, grid=grid)
+    for r in (0, 77, 127, 128, 129):
+        for b in range(in_f // 32):
+            S = float(grid[r // 128, (32 * b) // 128])
+            _exact_block_checks(W[r, 32 * b:32 * b + 32].tolist(), S, Q[r, 34 * b:34 * b + 34])
+    # the same bytes under a per-tensor scale equal to one tile's value give that tile's blocks
+    assert grid[0, 1] != grid[0, 0]
+    Q1 = oracle.requant_q8_0(W, in_f, in_f, out_f, scale=float(grid[0, 1]))
+    assert np.array_equal(Q1[:128, 34 * 4:34 * 8], Q[:128, 34 * 4:34 * 8])
+    assert not np.array_equal(Q1[:128, :34 * 4], Q[:128, :34 * 4])
+
+
+def test_requant_dequant_error_and_gemv_consistency():
+    out_f, in_f = 40, 512
+    W = synth.e4m3_weights(out_f, in_f)
+    S = 2.0 ** -4
+    Q = oracle.requant_q8_0(W, in_f, in_f, out_f, scale=S)
+    nb = in_f // 32
+    what = np.zeros((out_f, in_f))
+    wq = np.zeros((out_f, in_f))
+    err_bound = np.zeros((out_f, in_f))
+    for r in range(out_f):
+        for b in range(nb):
+            blk = Q[r, 34 * b:34 * b + 34]
+            d16 = oracle.fp16_value(int(blk[0]) | (int(blk[1]) << 8))
+            q = blk[2:].view(np.int8).astype(np.float64)
+            v = np.array([oracle.e4m3_value(c) for c in W[r, 32 * b:32 * b + 32]]) * S
+            d = np.abs(v).max() / 127
+            what[r, 32 * b:32 * b + 32] = v
+            wq[r, 32 * b:32 * b + 32] = d16 * q
+            err_bound[r, 32 * b:32 * b + 32] = d / 2 * (1 + 1e-6) + 127 * abs(d16 - d)
+    assert np.all(np.abs(wq - what) <= err_bound)
+    # the Q8_0 GEMV over the requantised rows differs from the e4m3 GEMV by at most the
+    # propagated dequantisation error
+    x = synth.x_rows(in_f, 1)
+    qs, dd = oracle.quantize_q8_1(x)
+    y8, _ = oracle.gemv_q8_0(Q, nb * 34, qs, dd, in_f, out_f)
+    ye, _ = oracle.gemv_e4m3(W, in_f, S, qs, dd, in_f, out_f)
+    a_hat = (np.repeat(dd.astype(np.float64), 32, axis=1) * qs.astype(np.float64))[0]
+    bound = (err_bound * np.abs(a_hat)).sum(axis=1)
+    assert np.all(np.abs(y8[0] - ye[0]) <= bound * (1 + 1e-9) + 1e-12)
+
+
+def test_requant_refuses_nan_and_bad_shapes():
+    W = np.zeros((1, 64), dtype=np.uint8)
+    W[0, 40] = 0x7F
+    with pytest.raises(ValueError):
+        oracle.requant_q8_0(W, 64, 64, 1, scale=1.0)
+    with pytest.raises(ValueError):
+        oracle.requant_q8_0(np.zeros((1, 64), np.uint8), 64, 64, 1, scale=float("inf"))
