@@ -489,6 +489,35 @@ def main() -> int:
                             "byte_ratio": 34 / 32}
             torch.cuda.empty_cache()
 
+    # Load-time e4m3 -> Q8_0 requantiser (gemv_e4m3_bench.rs, QUESTION: the ship path's Q8_0
+    # slab), per shape and scale kind: reads the e4m3 plane (and grid), writes the Q8_0 rows.
+    requant = {}
+    if not args.kernels_only:
+        for (out_f, in_f, a), obj in arm_objs.items():
+            if a not in ("e4m3", "blk128"):
+                continue
+            nbq = in_f // 32 * 34
+            Wq = [torch.empty(out_f * nbq, dtype=torch.uint8, device=dev) for _ in range(2)]
+            n = max(args.kernel_iters // 2, obj.copies)
+
+            def rq(i, obj=obj, a=a, Wq=Wq, nbq=nbq, out_f=out_f, in_f=in_f):
+                c = i % obj.copies
+                if a == "e4m3":
+                    fg.requant_e4m3_q8_0(obj.W[c], obj.row_bytes, SCALE, Wq[i % 2], nbq, in_f,
+                                         out_f)
+                else:
+                    fg.requant_e4m3_blk128_q8_0(obj.W[c], obj.row_bytes, obj.grids[c],
+                                                obj.grid_cols, Wq[i % 2], nbq, in_f, out_f)
+            g = capture(lambda: [rq(i) for i in range(n)])
+            g.replay()
+            us = timed(g.replay, n) * 1e3
+            moved = weight_bytes("e4m3", out_f, in_f) + grid_bytes(a, out_f, in_f) + out_f * nbq
+            requant[f"{a}@{out_f}x{in_f}"] = {"us": round(us, 3), "bytes": moved,
+                                              "GBs": round(moved / us / 1e3, 1),
+                                              "pct_peak": round(100 * moved / us / 1e3 / HBM_PEAK_GBS, 1)}
+            log(f"requant {a:6s} {out_f}x{in_f}: {us:8.2f} us  {moved / us / 1e3:7.1f} GB/s")
+            del g, Wq
+
     # Achievable read ceiling: the library's streaming-read measurement kernel over the same
     # rotated e4m3 copies (same bytes, same load pattern, no arithmetic).
     ceiling = {}
@@ -561,6 +590,7 @@ def main() -> int:
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
         "gemv": detail, "read_ceiling": ceiling, "m_rows": m_rows, "sheets": sheets,
+        "requant": requant,
         "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu,
     }

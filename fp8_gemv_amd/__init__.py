@@ -31,7 +31,8 @@ FP8GEMV_MAX_IN_F = 65536
 FP8GEMV_MAX_M = 65535
 
 EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "gemv_q8_0_q81", "gemv_e4m3_q81",
-           "gemv_e4m3_blk128_q81", "fp8gemv_read_bytes", "fp8gemv_strerror")
+           "gemv_e4m3_blk128_q81", "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
+           "fp8gemv_read_bytes", "fp8gemv_strerror")
 
 
 class Fp8GemvError(RuntimeError):
@@ -56,6 +57,8 @@ def _load() -> ctypes.CDLL:
         "gemv_q8_0_q81": [vp, i64, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_q81": [vp, i64, f32, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_blk128_q81": [vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, vp],
+        "requant_e4m3_q8_0": [vp, i64, f32, vp, i64, i32, i32, vp],
+        "requant_e4m3_blk128_q8_0": [vp, i64, vp, i32, vp, i64, i32, i32, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -197,6 +200,35 @@ def gemv_e4m3_blk128_q81(W, row_bytes: int, grid, grid_cols: int, qs, d, y, m: i
         _ptr(y, "y", torch.float32, m * out_f, dev),
         m, in_f, out_f, _stream(stream))
     _check("gemv_e4m3_blk128_q81", rc)
+
+
+# --------------------------------------------------------------------------- requantiser
+
+def _q_numel(q_row_bytes: int, out_f: int, in_f: int) -> int:
+    return (out_f - 1) * q_row_bytes + in_f // 32 * 34 if out_f >= 1 else 0
+
+
+def requant_e4m3_q8_0(W, row_bytes: int, scale: float, Wq, q_row_bytes: int, in_f: int,
+                      out_f: int, stream=None) -> None:
+    """Load-time e4m3 (per-tensor scale) -> Q8_0 rows in Wq (uint8)."""
+    dev = _dev(W)
+    rc = _lib.requant_e4m3_q8_0(_ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f),
+                                     dev), row_bytes, scale,
+                                _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev),
+                                q_row_bytes, in_f, out_f, _stream(stream))
+    _check("requant_e4m3_q8_0", rc)
+
+
+def requant_e4m3_blk128_q8_0(W, row_bytes: int, grid, grid_cols: int, Wq, q_row_bytes: int,
+                             in_f: int, out_f: int, stream=None) -> None:
+    """Load-time block-128 e4m3 -> Q8_0 rows in Wq (uint8)."""
+    dev = _dev(W)
+    rc = _lib.requant_e4m3_blk128_q8_0(
+        _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f), dev), row_bytes,
+        _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
+        _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev), q_row_bytes,
+        in_f, out_f, _stream(stream))
+    _check("requant_e4m3_blk128_q8_0", rc)
 
 
 def fp8gemv_read_bytes(buf, nbytes: int, sink, stream=None) -> None:

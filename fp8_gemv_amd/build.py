@@ -24,6 +24,7 @@ SOURCES = {
     "gemv_e4m3.hip": [],
     "gemv_q8_0.hip": [],
     "read_ceiling.hip": [],
+    "requant.hip": ["-ffp-contract=off"],
     "capi.hip": [],
 }
 

@@ -86,6 +86,39 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
                                              m, in_f, out_f, (hipStream_t)stream));
 }
 
+namespace {
+int check_requant(const uint8_t *W, int64_t row_bytes, void *Wq, int64_t q_row_bytes, int in_f,
+                  int out_f) {
+  if (!W || !Wq) return FP8GEMV_ERR_NULL;
+  if (out_f < 1 || bad_cols(in_f)) return FP8GEMV_ERR_SHAPE;
+  if (in_f > FP8GEMV_MAX_IN_F) return FP8GEMV_ERR_TOO_LARGE;
+  if (row_bytes < in_f || q_row_bytes < (int64_t)(in_f / 32) * 34) return FP8GEMV_ERR_ROW_BYTES;
+  if (!aligned(W, 16) || row_bytes % 16 != 0 || !aligned(Wq, 2) || q_row_bytes % 2 != 0)
+    return FP8GEMV_ERR_ALIGN;
+  return FP8GEMV_OK;
+}
+}  // namespace
+
+int requant_e4m3_q8_0(const uint8_t *W, int64_t row_bytes, float scale, void *Wq,
+                      int64_t q_row_bytes, int in_f, int out_f, void *stream) {
+  const int rc = check_requant(W, row_bytes, Wq, q_row_bytes, in_f, out_f);
+  if (rc) return rc;
+  return launch_rc(fp8gemv::launch_requant_q8_0(W, row_bytes, scale, nullptr, 0, false, Wq,
+                                                q_row_bytes, in_f, out_f, (hipStream_t)stream));
+}
+
+int requant_e4m3_blk128_q8_0(const uint8_t *W, int64_t row_bytes, const float *grid,
+                             int grid_cols, void *Wq, int64_t q_row_bytes, int in_f, int out_f,
+                             void *stream) {
+  const int rc = check_requant(W, row_bytes, Wq, q_row_bytes, in_f, out_f);
+  if (rc) return rc;
+  if (!grid) return FP8GEMV_ERR_NULL;
+  if (grid_cols != (in_f + 127) / 128) return FP8GEMV_ERR_GRID;
+  if (!aligned(grid, 4)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_requant_q8_0(W, row_bytes, 1.0f, grid, grid_cols, true, Wq,
+                                                q_row_bytes, in_f, out_f, (hipStream_t)stream));
+}
+
 int fp8gemv_read_bytes(const void *p, int64_t bytes, uint32_t *sink, void *stream) {
   if (!p || !sink) return FP8GEMV_ERR_NULL;
   if (bytes < 1) return FP8GEMV_ERR_SHAPE;

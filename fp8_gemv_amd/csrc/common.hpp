@@ -92,6 +92,9 @@ hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, co
                             float *y, int m, int in_f, int out_f, hipStream_t s);
 hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
                             const float *d, float *y, int m, int in_f, int out_f, hipStream_t s);
+hipError_t launch_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
+                               int grid_cols, bool blk128, void *Wq, int64_t q_row_bytes,
+                               int in_f, int out_f, hipStream_t s);
 hipError_t launch_read_bytes(const void *p, int64_t bytes, uint32_t *sink, hipStream_t s);
 
 }  // namespace fp8gemv

@@ -137,6 +137,39 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
                          void *stream);
 
 /*
+ * requant_e4m3_q8_0 -- load-time requantisation of a raw e4m3 weight plane (per-tensor scale)
+ * into ggml Q8_0 rows, the container gemv_q8_0_q81 reads.
+ * Source: gemv_e4m3_bench.rs, module doc QUESTION (the ship path dequantises FP8 checkpoints
+ * to a Q8_0 slab at load).  The page gives no formula; the rule is the q8_1 block rule with
+ * the scale stored as fp16.  Per 32-block b of row r, in f32:
+ *   v_i = e4m3(W[r, 32b + i]) * scale,  d = max|v_i| / 127,
+ *   q_i = round(v_i / d) with halves away from zero (0 when d == 0),
+ *   Wq[r] bytes 34b .. 34b+33 = binary16(d) (round to nearest even, little-endian), q_0..q_31.
+ *   W            u8 [out_f] rows of row_bytes bytes (first in_f used); 16-byte aligned,
+ *                row_bytes >= in_f and a multiple of 16
+ *   scale        finite (documented, not checked)
+ *   Wq           output rows of q_row_bytes bytes: only the first in_f / 32 * 34 bytes of each
+ *                row are written; 2-byte aligned, q_row_bytes >= in_f / 32 * 34 and even; must
+ *                not overlap W.  Wq 16-byte aligned with q_row_bytes % 16 == 0 and
+ *                in_f % 256 == 0 is the fastest layout (and the one the fast GEMV path needs).
+ *   in_f         multiple of 32, <= FP8GEMV_MAX_IN_F;  out_f >= 1
+ */
+int requant_e4m3_q8_0(const uint8_t *W, int64_t row_bytes, float scale, void *Wq,
+                      int64_t q_row_bytes, int in_f, int out_f, void *stream);
+
+/*
+ * requant_e4m3_blk128_q8_0 -- the same for a block-128 scaled plane: the block's S is
+ * grid[r / 128, b / 4] (each 32-block lies in one 128-column tile).
+ * Source: as above, plus THE BLOCK-128 ARM (the f32 [ceil(out_f/128), ceil(in_f/128)] grid).
+ *   grid       f32 [ceil(out_f/128), grid_cols], row-major, finite; 4-byte aligned
+ *   grid_cols  must equal ceil(in_f / 128)
+ *   other arguments as for requant_e4m3_q8_0
+ */
+int requant_e4m3_blk128_q8_0(const uint8_t *W, int64_t row_bytes, const float *grid,
+                             int grid_cols, void *Wq, int64_t q_row_bytes, int in_f, int out_f,
+                             void *stream);
+
+/*
  * fp8gemv_read_bytes -- measurement aid, not a step of the matvec: streams `bytes` bytes from
  * p with the GEMVs' load pattern (16-byte non-temporal loads, 1 KiB per wave-wide load,
  * 8 KiB per wave) and discards them; `sink` (one uint32) is written only in the

@@ -31,6 +31,7 @@ def fg():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1",
                                   "gemv_q8_0_q81", "gemv_e4m3_q81", "gemv_e4m3_blk128_q81",
+                                  "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
                                   "fp8gemv_read_bytes", "fp8gemv_strerror"])
 
 
@@ -114,6 +115,27 @@ def test_gemv_argument_errors(fg):
     assert L.gemv_q8_0_q81(FAKE + 1, 68, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
     assert L.gemv_q8_0_q81(FAKE, 69, FAKE, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
     assert L.gemv_q8_0_q81(FAKE, 68, FAKE + 4, FAKE, FAKE, 1, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+
+
+def test_requant_argument_errors(fg):
+    L, e = fg.lib(), fg
+    assert L.requant_e4m3_q8_0(None, 64, 1.0, FAKE, 68, 64, 8, None) == e.FP8GEMV_ERR_NULL
+    assert L.requant_e4m3_q8_0(FAKE, 64, 1.0, None, 68, 64, 8, None) == e.FP8GEMV_ERR_NULL
+    assert L.requant_e4m3_blk128_q8_0(FAKE, 64, None, 1, FAKE, 68, 64, 8, None) == e.FP8GEMV_ERR_NULL
+    assert L.requant_e4m3_q8_0(FAKE, 64, 1.0, FAKE, 68, 48, 8, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.requant_e4m3_q8_0(FAKE, 64, 1.0, FAKE, 68, 64, 0, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.requant_e4m3_q8_0(FAKE, 2 ** 17, 1.0, FAKE, 2 ** 17 // 32 * 34, 2 ** 17, 8,
+                               None) == e.FP8GEMV_ERR_TOO_LARGE
+    assert L.requant_e4m3_q8_0(FAKE, 48, 1.0, FAKE, 68, 64, 8, None) == e.FP8GEMV_ERR_ROW_BYTES
+    assert L.requant_e4m3_q8_0(FAKE, 64, 1.0, FAKE, 66, 64, 8, None) == e.FP8GEMV_ERR_ROW_BYTES
+    assert L.requant_e4m3_blk128_q8_0(FAKE, 256, FAKE, 1, FAKE, 272, 256, 8,
+                                      None) == e.FP8GEMV_ERR_GRID
+    assert L.requant_e4m3_q8_0(FAKE + 8, 64, 1.0, FAKE, 68, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.requant_e4m3_q8_0(FAKE, 72, 1.0, FAKE, 68, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.requant_e4m3_q8_0(FAKE, 64, 1.0, FAKE + 1, 68, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.requant_e4m3_q8_0(FAKE, 64, 1.0, FAKE, 69, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.requant_e4m3_blk128_q8_0(FAKE, 64, FAKE + 2, 1, FAKE, 68, 64, 8,
+                                      None) == e.FP8GEMV_ERR_ALIGN
 
 
 def test_read_bytes_argument_errors(fg):
