@@ -15,6 +15,8 @@ What it computes (docs.rs pages of memra-engine 0.125.0):
   in f32 -- see ``oracle.c``.
 * The three GEMVs of the bench page (src/bin/gemv_e4m3_bench.rs, module doc THE COMPARISON
   and THE BLOCK-128 ARM), f64 terms and sums -- see ``oracle.c``.
+* The SiLU-gated producer silu(gate) * up -> q8_1 (gate page, ``main``: the MoE expert-ff
+  site), in f64 with one rounding to f32, then the q8_1 step -- see ``oracle.c``.
 * The load-time e4m3 -> Q8_0 requantisation the same page names as its ship path (QUESTION),
   in f32 with an fp16 block scale -- see ``oracle.c`` for the reading it takes.
 
@@ -67,6 +69,8 @@ def _load():
         lib.oracle_gemv_e4m3_blk128.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, i32, i32,
                                                 i32, vp, vp]
         lib.oracle_gemv_e4m3_blk128.restype = i32
+        lib.oracle_silu_mul.argtypes = [vp, vp, i32, vp, vp]
+        lib.oracle_silu_mul.restype = None
         lib.oracle_f32_to_fp16.argtypes = [ctypes.c_float]
         lib.oracle_f32_to_fp16.restype = ctypes.c_uint16
         lib.oracle_requant_q8_0.argtypes = [vp, i64, f32, vp, i32, vp, i64, i32, i32, i32, i32]
@@ -92,6 +96,24 @@ def fp16_value(bits: int) -> float:
 
 
 # ------------------------------------------------------------------------- producer
+
+def silu_mul(gate: np.ndarray, up: np.ndarray):
+    """h = silu(gate) * up: returns (h64, h32) with the shape of gate."""
+    g = _c(gate, np.float32)
+    u = _c(up, np.float32)
+    assert g.shape == u.shape
+    h64 = np.empty(g.shape, dtype=np.float64)
+    h32 = np.empty(g.shape, dtype=np.float32)
+    _load().oracle_silu_mul(g.ctypes.data, u.ctypes.data, g.size, h64.ctypes.data,
+                            h32.ctypes.data)
+    return h64, h32
+
+
+def silu_mul_q8_1(gate: np.ndarray, up: np.ndarray):
+    """The SiLU-gated chain: silu_mul then q8_1 of the f32 rows."""
+    h64, h32 = silu_mul(gate, up)
+    qs, d = quantize_q8_1(np.atleast_2d(h32))
+    return {"h64": h64, "h32": h32, "qs": qs, "d": d}
 
 def rms_norm(x: np.ndarray, w: np.ndarray, eps: float = EPS):
     """RMSNorm of f32 rows x [nrows, ncols] with gain w [ncols].

@@ -273,3 +273,20 @@ int oracle_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const 
     }
     return 0;
 }
+
+/* ------------------------------------------------------- SiLU-gated producer ---- */
+
+/* h = silu(gate) * up for n values (q8_fuse_gate.rs `main`: the MoE expert-ff site's
+ * silu/gate*up -> q8_1 producer; the page names the operation, not a formula).  The standard
+ * SiLU-gated product, every step in f64 with libm exp, one rounding to f32:
+ *   h64 = (g / (1 + exp(-g))) * u,   h32 = (float)h64.
+ * The q8_1 step that follows is oracle_quantize_q8_1 on h32. */
+void oracle_silu_mul(const float *gate, const float *up, int n, double *h64, float *h32) {
+    for (int i = 0; i < n; ++i) {
+        double g = (double)gate[i];
+        double sg = g / (1.0 + exp(-g));
+        double h = sg * (double)up[i];
+        h64[i] = h;
+        h32[i] = (float)h;
+    }
+}

@@ -475,3 +475,45 @@ def test_requant_refuses_nan_and_bad_shapes():
         oracle.requant_q8_0(W, 64, 64, 1, scale=1.0)
     with pytest.raises(ValueError):
         oracle.requant_q8_0(np.zeros((1, 64), np.uint8), 64, 64, 1, scale=float("inf"))
+
+
+# --------------------------------------------------------------- SiLU-gated producer
+# silu(gate) * up (q8_fuse_gate.rs `main`: the MoE expert-ff activation site).  Pinned by
+# torch's silu, high-precision Decimal evaluation, the odd-part identity and exact scaling.
+
+def test_silu_mul_against_torch_f64():
+    g = synth.f32(11, 4096)
+    u = synth.f32(12, 4096)
+    h64, h32 = oracle.silu_mul(g, u)
+    ref = (torch.nn.functional.silu(torch.from_numpy(g.astype(np.float64))) *
+           torch.from_numpy(u.astype(np.float64))).numpy()
+    assert np.allclose(h64, ref, rtol=4e-16, atol=0)
+    assert np.array_equal(h32, h64.astype(np.float32))
+
+
+def test_silu_mul_closed_forms_decimal():
+    getcontext().prec = 60
+    gs = np.array([0.0, 1.0, -1.0, 0.5, -3.75, 3.9999998, -0.0009765625, 20.0, -20.0, 40.0],
+                  dtype=np.float32)
+    us = np.array([1.0, 2.0, -0.75, 3.0, 1.0, -4.0, 1.5, 1.0, 1.0, 0.25], dtype=np.float32)
+    h64, _ = oracle.silu_mul(gs, us)
+    for g, u, h in zip(gs.tolist(), us.tolist(), h64.tolist()):
+        gd = Decimal(g)
+        want = gd / (1 + (-gd).exp()) * Decimal(u)
+        if want == 0:
+            assert h == 0.0
+        else:
+            assert abs(Decimal(h) - want) <= abs(want) * Decimal(2) ** -50, (g, u, h, want)
+
+
+def test_silu_odd_part_identity_and_scaling():
+    g = synth.f32(13, 2048)
+    one = np.ones_like(g)
+    hp, _ = oracle.silu_mul(g, one)
+    hn, _ = oracle.silu_mul(-g, one)
+    # silu(g) - silu(-g) = g
+    assert np.allclose(hp - hn, g.astype(np.float64), rtol=1e-14, atol=1e-15)
+    u = synth.f32(14, 2048)
+    h1, _ = oracle.silu_mul(g, u)
+    h2, _ = oracle.silu_mul(g, 2 * u)  # doubling is exact in f32 and f64
+    assert np.array_equal(h2, 2 * h1)
