@@ -560,6 +560,26 @@ def main() -> int:
             g.replay()
             prod_us[f"{variant}@{ncols}"] = round(timed(g.replay, 50) * 1e3, 3)
 
+    # SiLU-gated producer at the page's expert-ff width (fused vs two-launch chain).
+    if not args.kernels_only:
+        ncols = 1536
+        gt = torch.from_numpy(synth.f32(0xA5A5 ^ ncols, ncols)).to(dev)
+        ut = torch.from_numpy(synth.f32(0x5A5A ^ ncols, ncols)).to(dev)
+        h = torch.empty(ncols, device=dev)
+        qs = torch.empty(ncols, dtype=torch.int8, device=dev)
+        d = torch.empty(ncols // 32, device=dev)
+        for variant in ("fused", "chain"):
+            def run():
+                if variant == "fused":
+                    fg.silu_mul_q8_1(gt, ut, h, qs, d, ncols, 1)
+                else:
+                    fg.silu_mul_f32(gt, ut, h, ncols, 1)
+                    fg.quantize_q8_1(h, qs, d, 1, ncols)
+            run()
+            g = capture(lambda: [run() for _ in range(50)])
+            g.replay()
+            prod_us[f"silu_{variant}@{ncols}"] = round(timed(g.replay, 50) * 1e3, 3)
+
     # Roofline of the dominant GEMV kernel (largest time per step).
     dom_key = max(detail, key=lambda k: detail[k]["us"])
     dom = detail[dom_key]

@@ -30,7 +30,8 @@ FP8GEMV_ERR_TOO_LARGE = -6
 FP8GEMV_MAX_IN_F = 65536
 FP8GEMV_MAX_M = 65535
 
-EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "gemv_q8_0_q81", "gemv_e4m3_q81",
+EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "silu_mul_f32", "silu_mul_q8_1",
+           "gemv_q8_0_q81", "gemv_e4m3_q81",
            "gemv_e4m3_blk128_q81", "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
            "fp8gemv_read_bytes", "fp8gemv_strerror")
 
@@ -54,6 +55,8 @@ def _load() -> ctypes.CDLL:
         "rms_norm_f32": [vp, vp, vp, i32, i32, f32, vp],
         "quantize_q8_1": [vp, vp, vp, i32, i32, vp],
         "rmsnorm_q8_1": [vp, vp, vp, vp, vp, i32, i32, f32, vp],
+        "silu_mul_f32": [vp, vp, vp, i32, i32, vp],
+        "silu_mul_q8_1": [vp, vp, vp, vp, vp, i32, i32, vp],
         "gemv_q8_0_q81": [vp, i64, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_q81": [vp, i64, f32, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_blk128_q81": [vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, vp],
@@ -151,6 +154,29 @@ def rmsnorm_q8_1(x, w, z, qs, d, ncols: int, nrows: int, eps: float = 1e-6,
                            _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
                            ncols, nrows, eps, _stream(stream))
     _check("rmsnorm_q8_1", rc)
+
+
+def silu_mul_f32(gate, up, h, ncols: int, nrows: int, stream=None) -> None:
+    """h = silu(gate) * up (first half of the SiLU-gated chain)."""
+    dev = _dev(gate)
+    n = ncols * nrows
+    rc = _lib.silu_mul_f32(_ptr(gate, "gate", torch.float32, n, dev),
+                           _ptr(up, "up", torch.float32, n, dev),
+                           _ptr(h, "h", torch.float32, n, dev), ncols, nrows, _stream(stream))
+    _check("silu_mul_f32", rc)
+
+
+def silu_mul_q8_1(gate, up, h, qs, d, ncols: int, nrows: int, stream=None) -> None:
+    """Fused SiLU-gated producer: silu(gate) * up then q8_1 in one launch (h may be None)."""
+    dev = _dev(gate)
+    n = ncols * nrows
+    rc = _lib.silu_mul_q8_1(_ptr(gate, "gate", torch.float32, n, dev),
+                            _ptr(up, "up", torch.float32, n, dev),
+                            _ptr(h, "h", torch.float32, n, dev),
+                            _ptr(qs, "qs", torch.int8, n, dev),
+                            _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
+                            ncols, nrows, _stream(stream))
+    _check("silu_mul_q8_1", rc)
 
 
 # -------------------------------------------------------------------------------- GEMVs

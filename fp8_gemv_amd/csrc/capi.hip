@@ -53,6 +53,27 @@ int rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d,
       fp8gemv::launch_rmsnorm_q8_1(x, w, z, qs, d, ncols, nrows, eps, (hipStream_t)stream));
 }
 
+int silu_mul_f32(const float *gate, const float *up, float *h, int ncols, int nrows,
+                 void *stream) {
+  if (!gate || !up || !h) return FP8GEMV_ERR_NULL;
+  if (nrows < 1 || bad_cols(ncols)) return FP8GEMV_ERR_SHAPE;
+  if (ncols > FP8GEMV_MAX_IN_F || nrows > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(h, 16)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_silu_mul(gate, up, h, ncols, nrows, (hipStream_t)stream));
+}
+
+int silu_mul_q8_1(const float *gate, const float *up, float *h, int8_t *qs, float *d, int ncols,
+                  int nrows, void *stream) {
+  if (!gate || !up || !qs || !d) return FP8GEMV_ERR_NULL;
+  if (nrows < 1 || bad_cols(ncols)) return FP8GEMV_ERR_SHAPE;
+  if (ncols > FP8GEMV_MAX_IN_F || nrows > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(gate, 16) || !aligned(up, 16) || (h && !aligned(h, 16)) || !aligned(qs, 16) ||
+      !aligned(d, 4))
+    return FP8GEMV_ERR_ALIGN;
+  return launch_rc(
+      fp8gemv::launch_silu_mul_q8_1(gate, up, h, qs, d, ncols, nrows, (hipStream_t)stream));
+}
+
 int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
                   int m, int in_f, int out_f, void *stream) {
   const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);

@@ -87,6 +87,10 @@ hipError_t launch_quantize_q8_1(const float *z, int8_t *qs, float *d, int nrows,
                                 hipStream_t s);
 hipError_t launch_rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d,
                                int ncols, int nrows, float eps, hipStream_t s);
+hipError_t launch_silu_mul(const float *g, const float *u, float *h, int ncols, int nrows,
+                           hipStream_t s);
+hipError_t launch_silu_mul_q8_1(const float *g, const float *u, float *h, int8_t *qs, float *d,
+                                int ncols, int nrows, hipStream_t s);
 hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                             int grid_cols, bool blk128, const int8_t *qs, const float *d,
                             float *y, int m, int in_f, int out_f, hipStream_t s);

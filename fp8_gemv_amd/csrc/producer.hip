@@ -19,6 +19,12 @@
 //   s   = 1 / sqrt(ss / ncols + eps)                        (f64, IEEE div and sqrt)
 //   z_j = (float)(((double)x_j * (double)w_j) * s)          (x_j * w_j is exact in f64)
 //   q8_1 per 32-block in f32: d = amax / 127, id = d ? 1 / d : 0, q = roundf(z * id).
+//
+// The second front end, silu(gate) * up -> q8_1 (the same page's main: the MoE expert-ff
+// width 1536 is the activation fusion site still on the unfused chain), follows the same
+// pattern: a chain (silu_mul_f32 then quantize_q8_1) and a fused kernel sharing the device
+// function h_value, byte-identical by construction.  h_value in f64, rounded once to f32:
+//   h_j = (float)((g_j / (1 + exp(-g_j))) * u_j)            (g, u widened exactly to f64)
 #include "common.hpp"
 
 namespace fp8gemv {
@@ -88,6 +94,13 @@ __device__ double row_scale(const float *__restrict__ x, int ncols, float eps, d
 
 __device__ __forceinline__ float z_value(float x, float w, double s) {
   return (float)(((double)x * (double)w) * s);
+}
+
+// SiLU-gated product of one column, in f64 with a single rounding to f32.
+__device__ __forceinline__ float h_value(float g, float u) {
+  const double gd = (double)g;
+  const double sg = gd / (1.0 + exp(-gd));
+  return (float)(sg * (double)u);
 }
 
 // q8_1 of one 32-block held by 8 consecutive lanes (4 values each).  All 8 lanes of a group
@@ -182,7 +195,62 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm_q8_1(const float *__restri
   }
 }
 
+__global__ __launch_bounds__(kThreads) void k_silu_mul(const float *__restrict__ g,
+                                                       const float *__restrict__ u,
+                                                       float *__restrict__ h, int ncols) {
+  const int64_t row = blockIdx.y;
+  const int j = blockIdx.x * kColsPerPass + threadIdx.x * 4;
+  if (j < ncols) {
+    const float4 gv = *reinterpret_cast<const float4 *>(g + row * ncols + j);
+    const float4 uv = *reinterpret_cast<const float4 *>(u + row * ncols + j);
+    *reinterpret_cast<float4 *>(h + row * ncols + j) =
+        make_float4(h_value(gv.x, uv.x), h_value(gv.y, uv.y), h_value(gv.z, uv.z),
+                    h_value(gv.w, uv.w));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_silu_mul_q8_1(const float *__restrict__ g,
+                                                            const float *__restrict__ u,
+                                                            float *__restrict__ h,
+                                                            int8_t *__restrict__ qs,
+                                                            float *__restrict__ d, int ncols) {
+  const int64_t row = blockIdx.y;
+  const int j = blockIdx.x * kColsPerPass + threadIdx.x * 4;
+  const bool live = j < ncols;  // whole 8-lane groups are live or not (ncols % 32 == 0)
+  float hv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const float4 gv = *reinterpret_cast<const float4 *>(g + row * ncols + j);
+    const float4 uv = *reinterpret_cast<const float4 *>(u + row * ncols + j);
+    hv[0] = h_value(gv.x, uv.x);
+    hv[1] = h_value(gv.y, uv.y);
+    hv[2] = h_value(gv.z, uv.z);
+    hv[3] = h_value(gv.w, uv.w);
+    if (h != nullptr)
+      *reinterpret_cast<float4 *>(h + row * ncols + j) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+  }
+  float db;
+  const uint32_t packed = quant_group(hv, db);
+  if (live) {
+    *reinterpret_cast<uint32_t *>(qs + row * ncols + j) = packed;
+    if ((threadIdx.x & 7) == 0) d[row * (ncols / 32) + j / 32] = db;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_silu_mul(const float *g, const float *u, float *h, int ncols, int nrows,
+                           hipStream_t s) {
+  const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
+  hipLaunchKernelGGL(k_silu_mul, grid, dim3(kThreads), 0, s, g, u, h, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_q8_1(const float *g, const float *u, float *h, int8_t *qs, float *d,
+                                int ncols, int nrows, hipStream_t s) {
+  const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
+  hipLaunchKernelGGL(k_silu_mul_q8_1, grid, dim3(kThreads), 0, s, g, u, h, qs, d, ncols);
+  return hipGetLastError();
+}
 
 hipError_t launch_rms_norm(const float *x, const float *w, float *z, int ncols, int nrows,
                            float eps, hipStream_t s) {

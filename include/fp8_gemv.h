@@ -92,6 +92,29 @@ int rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t *qs, float *d,
                  int nrows, float eps, void *stream);
 
 /*
+ * silu_mul_f32 -- first half of the SiLU-gated producer chain: h = silu(gate) * up.
+ * Source: q8_fuse_gate.rs, `main` (the MoE expert-ff width n_ff_exp = 1536 is the activation
+ * fusion site, silu/gate*up -> q8_1, still on the unfused chain).  The page names the
+ * operation and gives no formula; the rule is the standard SiLU-gated product:
+ *   h[r, j] = (float)((g / (1 + exp(-g))) * u)  with g = gate[r, j], u = up[r, j] widened to
+ *   f64, every step in f64, one rounding to f32 at the end.
+ *   gate, up, h   f32 [nrows, ncols], 16-byte aligned; h may not alias gate or up
+ *   ncols multiple of 32, <= FP8GEMV_MAX_IN_F; 1 <= nrows <= FP8GEMV_MAX_M
+ * The chain is silu_mul_f32 then quantize_q8_1.
+ */
+int silu_mul_f32(const float *gate, const float *up, float *h, int ncols, int nrows,
+                 void *stream);
+
+/*
+ * silu_mul_q8_1 -- the fused SiLU-gated producer: silu_mul_f32 then quantize_q8_1 in one
+ * launch, byte-identical in h, qs and d to that chain.  h may be NULL (not stored).
+ * Source: as above, with the fused-producer contract of q8_fuse_gate.rs's module doc.
+ *   qs int8 [nrows, ncols] (16-byte aligned), d f32 [nrows, ncols / 32] (4-byte aligned)
+ */
+int silu_mul_q8_1(const float *gate, const float *up, float *h, int8_t *qs, float *d, int ncols,
+                  int nrows, void *stream);
+
+/*
  * gemv_q8_0_q81 -- matvec over ggml Q8_0 weight rows.
  * Source: gemv_e4m3_bench.rs, QUESTION and THE COMPARISON (arm Q8_0: 34 bytes per 32
  * weights, an fp16 scale then 32 int8, row_bytes = in_f / 32 * 34) and `synth_q8_0`.

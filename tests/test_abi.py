@@ -30,6 +30,7 @@ def fg():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1",
+                                  "silu_mul_f32", "silu_mul_q8_1",
                                   "gemv_q8_0_q81", "gemv_e4m3_q81", "gemv_e4m3_blk128_q81",
                                   "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
                                   "fp8gemv_read_bytes", "fp8gemv_strerror"])
@@ -84,6 +85,19 @@ def test_producer_argument_errors(fg):
     assert L.rmsnorm_q8_1(FAKE, FAKE, None, None, FAKE, 64, 1, 1e-6, None) == fg.FP8GEMV_ERR_NULL
     assert L.rmsnorm_q8_1(FAKE, FAKE, None, FAKE, FAKE, 33, 1, 1e-6, None) == fg.FP8GEMV_ERR_SHAPE
     assert L.rmsnorm_q8_1(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 64, 1, 1e-6, None) == fg.FP8GEMV_ERR_ALIGN
+
+
+def test_silu_producer_argument_errors(fg):
+    L, e = fg.lib(), fg
+    assert L.silu_mul_f32(None, FAKE, FAKE, 64, 1, None) == e.FP8GEMV_ERR_NULL
+    assert L.silu_mul_f32(FAKE, FAKE, FAKE, 40, 1, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.silu_mul_f32(FAKE, FAKE, FAKE, 64, 0, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.silu_mul_f32(FAKE, FAKE, FAKE, 65536 + 32, 1, None) == e.FP8GEMV_ERR_TOO_LARGE
+    assert L.silu_mul_f32(FAKE, FAKE + 4, FAKE, 64, 1, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.silu_mul_q8_1(FAKE, FAKE, None, None, FAKE, 64, 1, None) == e.FP8GEMV_ERR_NULL
+    assert L.silu_mul_q8_1(FAKE, FAKE, None, FAKE, FAKE, 33, 1, None) == e.FP8GEMV_ERR_SHAPE
+    assert L.silu_mul_q8_1(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 64, 1, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.silu_mul_q8_1(FAKE, FAKE, None, FAKE, FAKE + 2, 64, 1, None) == e.FP8GEMV_ERR_ALIGN
 
 
 def test_gemv_argument_errors(fg):
