@@ -98,6 +98,9 @@ class Arm:
     def launch(self, qs, d, m=1):
         c = self.i % self.copies
         self.i += 1
+        self.launch_copy(qs, d, c, m)
+
+    def launch_copy(self, qs, d, c, m=1):
         fg = self.fg
         if self.arm == "q8_0":
             fg.gemv_q8_0_q81(self.W[c], self.row_bytes, qs, d, self.y, m, self.in_f, self.out_f)
@@ -109,8 +112,38 @@ class Arm:
                                     d, self.y, m, self.in_f, self.out_f)
 
 
-def cpu_baseline(shapes, arms, threads: int):
-    """The oracle, as it stands, over one full step on `threads` host threads (row ranges)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def gpu_state() -> dict:
+    """Current clocks and temperatures of the GPU, from rocm-smi run as a child process."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showtemp", "-c", "--json"], capture_output=True,
+                             text=True, timeout=30).stdout
+        cards = json.loads(out)
+        card = cards[sorted(k for k in cards if k.startswith("card"))[0]]
+        keep = {}
+        for k, v in card.items():
+            kl = k.lower()
+            if "temperature" in kl or kl.startswith("sclk") or kl.startswith("mclk") or \
+                    kl.startswith("fclk") or kl.startswith("socclk"):
+                keep[k] = v
+        return keep
+    except Exception as e:  # noqa: BLE001 -- a missing tool must not stop the bench
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def cpu_baseline(shapes, arms, threads: int, reps: int = 3):
+    """The oracle, as it stands, over one full step on `threads` host threads (row ranges),
+    `reps` times (median); plus the same step's 5120x5120 part on one thread."""
     import oracle
     import synth
     work = []
@@ -129,26 +162,35 @@ def cpu_baseline(shapes, arms, threads: int):
             return oracle.gemv_e4m3(W, in_f, SCALE, qs, d, in_f, out_f, rows)
         return oracle.gemv_e4m3_blk128(W, in_f, g, qs, d, in_f, out_f, rows)
 
-    t0 = time.perf_counter()
-    wbytes = 0
-    acts = {}
-    for arm, out_f, in_f, x, w, W, g in work:
-        if (out_f, in_f) not in acts:
-            ref = oracle.rmsnorm_q8_1(x, w)
-            acts[(out_f, in_f)] = (ref["qs"], ref["d"])
-        qs, d = acts[(out_f, in_f)]
-        step = (out_f + threads - 1) // threads
-        futs = [pool.submit(gemv, arm, out_f, in_f, W, g, qs, d, (r, min(out_f, r + step)))
-                for r in range(0, out_f, step)]
-        for f in futs:
-            f.result()
-        wbytes += weight_bytes(arm, out_f, in_f)
-    secs = time.perf_counter() - t0
+    def one_step(items, nthreads):
+        t0 = time.perf_counter()
+        wbytes = 0
+        acts = {}
+        for arm, out_f, in_f, x, w, W, g in items:
+            if (out_f, in_f) not in acts:
+                ref = oracle.rmsnorm_q8_1(x, w)
+                acts[(out_f, in_f)] = (ref["qs"], ref["d"])
+            qs, d = acts[(out_f, in_f)]
+            step = (out_f + nthreads - 1) // nthreads
+            futs = [pool.submit(gemv, arm, out_f, in_f, W, g, qs, d, (r, min(out_f, r + step)))
+                    for r in range(0, out_f, step)]
+            for f in futs:
+                f.result()
+            wbytes += weight_bytes(arm, out_f, in_f)
+        return wbytes, time.perf_counter() - t0
+
+    runs = [one_step(work, threads) for _ in range(reps)]
+    wbytes = runs[0][0]
+    secs = sorted(r[1] for r in runs)[len(runs) // 2]
+    small = [it for it in work if (it[1], it[2]) == (5120, 5120)] or work[:1]
+    wb1, secs1 = one_step(small, 1)
     pool.shutdown()
     return {"value": round(wbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "ms_per_step": round(secs * 1e3, 1),
-            "sample": "one full step: rmsnorm_q8_1 per shape + the 9 GEMVs (3 shapes x 3 containers), "
-                      "f64 oracle, output rows split over host threads"}
+            "single_thread_GBs": round(wb1 / secs1 / 1e9, 3), "cpu_model": cpu_model(),
+            "sample": f"one full step (rmsnorm_q8_1 per shape + the 9 GEMVs, 3 shapes x 3 "
+                      f"containers, f64 oracle, output rows split over {threads} host threads), "
+                      f"median of {reps}; single_thread_GBs: the 5120x5120 part on one thread"}
 
 
 # ------------------------------------------------------------------ profile summaries
@@ -310,6 +352,7 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    state_in = gpu_state()
     import torch
     import fp8_gemv_amd as fg
 
@@ -580,6 +623,50 @@ def main() -> int:
             g.replay()
             prod_us[f"silu_{variant}@{ncols}"] = round(timed(g.replay, 50) * 1e3, 3)
 
+    # DRAM-cold cross-checks on the 17408x5120 e4m3 launch (gemv_e4m3_bench.rs, DRAM-COLD
+    # DISCIPLINE): (a) per-launch time with 512 MB pushed through the device right before each
+    # launch must match the rotation's; (b) the time over a growing number of rotated copies
+    # must plateau once the rotation set exceeds the last-level cache.
+    cold = {}
+    key = (17408, 5120, "e4m3")
+    if key in arm_objs and not args.kernels_only:
+        obj = arm_objs[key]
+        qs, d = producer(key[:2])
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        # One launch at a time between its own events (so each includes its dispatch and
+        # ramp-up), right after either the scrub or a spin kernel of similar length that
+        # touches no memory (an idle GPU would lower its clocks); only the pair is comparable.
+        for label, scrub in (("spin_us_median", False), ("scrub_512MB_us_median", True)):
+            per = []
+            for i in range(24):
+                if scrub:
+                    dst.copy_(src)  # reads 256 MiB and writes 256 MiB
+                else:
+                    torch.cuda._sleep(200_000)  # ~0.1 ms of clock cycles, no memory traffic
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                obj.launch(qs, d)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3)
+            cold[label] = round(sorted(per)[len(per) // 2], 3)
+        del src, dst
+        sweep = {}
+        for c in sorted({1, 2, 4, obj.copies}):
+            if c > obj.copies:
+                continue
+            n = max(args.kernel_iters, c)
+            g = capture(lambda: [obj.launch_copy(qs, d, i % c) for i in range(n)])
+            g.replay()
+            sweep[str(c)] = round(timed(g.replay, n) * 1e3, 3)
+        cold["copies_us"] = sweep
+        cold["rotation_us"] = detail.get("e4m3@17408x5120", {}).get("us")
+        cold["copy_bytes"] = weight_bytes("e4m3", 17408, 5120)
+        log(f"cold check: after spin {cold['spin_us_median']} us, after scrub "
+            f"{cold['scrub_512MB_us_median']} us, copies {sweep}")
+
     # Roofline of the dominant GEMV kernel (largest time per step).
     dom_key = max(detail, key=lambda k: detail[k]["us"])
     dom = detail[dom_key]
@@ -612,7 +699,8 @@ def main() -> int:
         "gemv": detail, "read_ceiling": ceiling, "m_rows": m_rows, "sheets": sheets,
         "requant": requant,
         "producer_us": prod_us,
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "cold_check": cold,
+        "gpu_state": {"entry": state_in, "exit": gpu_state()},
     }
     print(json.dumps(out), flush=True)
     return 0
