@@ -279,6 +279,52 @@ def test_graph_replays_match_eager(fg):
         torch.cuda.synchronize()
 
 
+def test_graph_replays_of_the_other_entry_points(fg):
+    # The two-launch chains, the SiLU-gated producer, m = 4 rows and the requantiser under
+    # graph replay: every replay, with eager work between replays, reproduces the eager bytes.
+    case("graph replay of chains, silu producer, m = 4 and requant")
+    in_f, out_f = 2048, 384
+    x = to_dev(synth.x_rows(in_f, 4))
+    w = to_dev(synth.gain(in_f))
+    gate, up = to_dev(synth.f32(5, in_f)), to_dev(synth.f32(6, in_f))
+    z = torch.empty((4, in_f), device=dev())
+    qs = torch.empty((4, in_f), dtype=torch.int8, device=dev())
+    d = torch.empty((4, in_f // 32), device=dev())
+    h = torch.empty(in_f, device=dev())
+    hq = torch.empty(in_f, dtype=torch.int8, device=dev())
+    hd = torch.empty(in_f // 32, device=dev())
+    c = Case("blk128", out_f, in_f, 1)
+    y = torch.empty((4, out_f), device=dev())
+    Wq = torch.empty(out_f * in_f // 32 * 34, dtype=torch.uint8, device=dev())
+    yq = torch.empty((4, out_f), device=dev())
+    outs = [z, qs, d, h, hq, hd, y, Wq, yq]
+
+    def run():
+        fg.rms_norm_f32(x, w, z, in_f, 4)
+        fg.quantize_q8_1(z, qs, d, 4, in_f)
+        fg.silu_mul_q8_1(gate, up, h, hq, hd, in_f, 1)
+        fg.gemv_e4m3_blk128_q81(c.Wd, c.row_bytes, c.gd, c.grid.shape[1], qs, d, y, 4, in_f,
+                                out_f)
+        fg.requant_e4m3_blk128_q8_0(c.Wd, c.row_bytes, c.gd, c.grid.shape[1], Wq,
+                                    in_f // 32 * 34, in_f, out_f)
+        fg.gemv_q8_0_q81(Wq, in_f // 32 * 34, qs, d, yq, 4, in_f, out_f)
+
+    run()
+    eager = [host(t).copy() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        for e, t in zip(eager, outs):
+            assert e.tobytes() == host(t).tobytes(), rep
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_read_bytes_measurement_kernel_runs(fg):
     case("fp8gemv_read_bytes")
     buf = torch.randint(0, 255, (3 * 32768 + 48,), dtype=torch.uint8, device=dev())
