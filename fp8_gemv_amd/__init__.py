@@ -91,9 +91,10 @@ def _check(fn: str, rc: int) -> None:
         raise Fp8GemvError(fn, rc, strerror(rc))
 
 
-def _stream(stream) -> int:
+def _stream(stream, dev=None) -> int:
+    """The stream handle: the given one, else torch's current stream of the tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
@@ -129,7 +130,7 @@ def rms_norm_f32(x, w, z, ncols: int, nrows: int, eps: float = 1e-6, stream=None
     rc = _lib.rms_norm_f32(_ptr(x, "x", torch.float32, ncols * nrows, dev),
                            _ptr(w, "w", torch.float32, ncols, dev),
                            _ptr(z, "z", torch.float32, ncols * nrows, dev),
-                           ncols, nrows, eps, _stream(stream))
+                           ncols, nrows, eps, _stream(stream, dev))
     _check("rms_norm_f32", rc)
 
 
@@ -139,7 +140,7 @@ def quantize_q8_1(z, qs, d, nrows: int, ncols: int, stream=None) -> None:
     rc = _lib.quantize_q8_1(_ptr(z, "z", torch.float32, ncols * nrows, dev),
                             _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
                             _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
-                            nrows, ncols, _stream(stream))
+                            nrows, ncols, _stream(stream, dev))
     _check("quantize_q8_1", rc)
 
 
@@ -152,7 +153,7 @@ def rmsnorm_q8_1(x, w, z, qs, d, ncols: int, nrows: int, eps: float = 1e-6,
                            _ptr(z, "z", torch.float32, ncols * nrows, dev),
                            _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
                            _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
-                           ncols, nrows, eps, _stream(stream))
+                           ncols, nrows, eps, _stream(stream, dev))
     _check("rmsnorm_q8_1", rc)
 
 
@@ -162,7 +163,7 @@ def silu_mul_f32(gate, up, h, ncols: int, nrows: int, stream=None) -> None:
     n = ncols * nrows
     rc = _lib.silu_mul_f32(_ptr(gate, "gate", torch.float32, n, dev),
                            _ptr(up, "up", torch.float32, n, dev),
-                           _ptr(h, "h", torch.float32, n, dev), ncols, nrows, _stream(stream))
+                           _ptr(h, "h", torch.float32, n, dev), ncols, nrows, _stream(stream, dev))
     _check("silu_mul_f32", rc)
 
 
@@ -175,7 +176,7 @@ def silu_mul_q8_1(gate, up, h, qs, d, ncols: int, nrows: int, stream=None) -> No
                             _ptr(h, "h", torch.float32, n, dev),
                             _ptr(qs, "qs", torch.int8, n, dev),
                             _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
-                            ncols, nrows, _stream(stream))
+                            ncols, nrows, _stream(stream, dev))
     _check("silu_mul_q8_1", rc)
 
 
@@ -196,7 +197,7 @@ def gemv_q8_0_q81(W, row_bytes: int, qs, d, y, m: int, in_f: int, out_f: int,
                             _ptr(qs, "qs", torch.int8, m * in_f, dev),
                             _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
                             _ptr(y, "y", torch.float32, m * out_f, dev),
-                            m, in_f, out_f, _stream(stream))
+                            m, in_f, out_f, _stream(stream, dev))
     _check("gemv_q8_0_q81", rc)
 
 
@@ -210,7 +211,7 @@ def gemv_e4m3_q81(W, row_bytes: int, scale: float, qs, d, y, m: int, in_f: int, 
                             _ptr(qs, "qs", torch.int8, m * in_f, dev),
                             _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
                             _ptr(y, "y", torch.float32, m * out_f, dev),
-                            m, in_f, out_f, _stream(stream))
+                            m, in_f, out_f, _stream(stream, dev))
     _check("gemv_e4m3_q81", rc)
 
 
@@ -224,7 +225,7 @@ def gemv_e4m3_blk128_q81(W, row_bytes: int, grid, grid_cols: int, qs, d, y, m: i
         _ptr(qs, "qs", torch.int8, m * in_f, dev),
         _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
         _ptr(y, "y", torch.float32, m * out_f, dev),
-        m, in_f, out_f, _stream(stream))
+        m, in_f, out_f, _stream(stream, dev))
     _check("gemv_e4m3_blk128_q81", rc)
 
 
@@ -241,7 +242,7 @@ def requant_e4m3_q8_0(W, row_bytes: int, scale: float, Wq, q_row_bytes: int, in_
     rc = _lib.requant_e4m3_q8_0(_ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f),
                                      dev), row_bytes, scale,
                                 _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev),
-                                q_row_bytes, in_f, out_f, _stream(stream))
+                                q_row_bytes, in_f, out_f, _stream(stream, dev))
     _check("requant_e4m3_q8_0", rc)
 
 
@@ -253,7 +254,7 @@ def requant_e4m3_blk128_q8_0(W, row_bytes: int, grid, grid_cols: int, Wq, q_row_
         _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f), dev), row_bytes,
         _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
         _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev), q_row_bytes,
-        in_f, out_f, _stream(stream))
+        in_f, out_f, _stream(stream, dev))
     _check("requant_e4m3_blk128_q8_0", rc)
 
 
@@ -261,7 +262,7 @@ def fp8gemv_read_bytes(buf, nbytes: int, sink, stream=None) -> None:
     """Measurement aid: stream nbytes of buf with the GEMVs' load pattern (no result)."""
     dev = _dev(buf)
     rc = _lib.fp8gemv_read_bytes(_ptr(buf, "buf", torch.uint8, nbytes, dev), nbytes,
-                                 _ptr(sink, "sink", torch.int32, 1, dev), _stream(stream))
+                                 _ptr(sink, "sink", torch.int32, 1, dev), _stream(stream, dev))
     _check("fp8gemv_read_bytes", rc)
 
 

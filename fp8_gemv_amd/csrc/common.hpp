@@ -76,6 +76,27 @@ __device__ __forceinline__ int wave_id() {
 
 }  // namespace fp8gemv
 
+// ------------------------------------------------------------- launch-time helpers ----
+// Raise a kernel's dynamic LDS limit to `bytes` once per device (the attribute is per device).
+// Thread-safe: concurrent first calls may both set it, which is harmless; the result is
+// remembered only when it succeeded.
+#include <atomic>
+namespace fp8gemv {
+constexpr int kMaxDevices = 64;
+inline hipError_t set_lds_limit_once(const void *kernel, size_t bytes,
+                                     std::atomic<bool> (&done)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire))
+    return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices)
+    done[dev].store(true, std::memory_order_release);
+  return e;
+}
+}  // namespace fp8gemv
+
 // --------------------------------------------------------------- internal launchers ----
 // Host-side launchers, one per kernel family; arguments are validated by the C ABI layer
 // before these run.  Each returns the hipError_t of the launch.

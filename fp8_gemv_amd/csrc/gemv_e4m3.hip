@@ -306,15 +306,11 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
                       int grid_cols, const int8_t *qs, const float *d, float *y, int m,
                       int in_f, int out_f, hipStream_t s) {
   auto kern = k_gemv_e4m3<BLK, C>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const size_t want = C::MT * act_lds_bytes(C::MAX_IN_F) + kSinkBytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(want < kLdsBytes ? want : kLdsBytes));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const size_t want = C::MT * act_lds_bytes(C::MAX_IN_F) + kSinkBytes;
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void *>(kern),
+                                          want < kLdsBytes ? want : kLdsBytes, lds_set);
+  if (e != hipSuccess) return e;
   const dim3 g((out_f + C::ROWS - 1) / C::ROWS, (m + C::MT - 1) / C::MT);
   hipLaunchKernelGGL(kern, g, dim3(C::THREADS), C::MT * act_lds_bytes(in_f) + kSinkBytes, s, W,
                      row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f);

@@ -383,15 +383,11 @@ template <class C>
 hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, const float *d,
                        float *y, int m, int in_f, int out_f, hipStream_t s) {
   auto kern = k_gemv_q8_0_fast<C>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const size_t want = fast_lds_bytes(C::MAX_IN_F, C::MT);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(want < kLdsBytes ? want : kLdsBytes));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const size_t want = fast_lds_bytes(C::MAX_IN_F, C::MT);
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void *>(kern),
+                                          want < kLdsBytes ? want : kLdsBytes, lds_set);
+  if (e != hipSuccess) return e;
   const dim3 g((out_f + C::ROWS - 1) / C::ROWS, (m + C::MT - 1) / C::MT);
   hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes(in_f, C::MT), s, W, row_bytes, qs,
                      d, y, m, in_f, out_f);

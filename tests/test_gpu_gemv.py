@@ -332,3 +332,25 @@ def test_read_bytes_measurement_kernel_runs(fg):
     for nbytes in (16, 1000 * 16, buf.numel()):
         fg.fp8gemv_read_bytes(buf, nbytes, sink)
     assert int(host(sink)[0]) == 7
+
+
+def test_calls_on_an_explicit_stream_are_ordered_on_it(fg):
+    # Every entry point takes the caller's stream: a producer -> GEMV chain issued on a
+    # non-default stream runs there in order and matches the same chain on the default one.
+    case("explicit stream")
+    in_f, out_f = 4096, 1000
+    x = to_dev(synth.x_rows(in_f, 1))
+    w = to_dev(synth.gain(in_f))
+    c = Case("q8_0", out_f, in_f, 1)
+    outs = []
+    for use_side in (False, True):
+        s = torch.cuda.Stream() if use_side else torch.cuda.current_stream()
+        qs = torch.empty(in_f, dtype=torch.int8, device=dev())
+        d = torch.empty(in_f // 32, device=dev())
+        y = torch.empty(out_f, device=dev())
+        torch.cuda.synchronize()
+        fg.rmsnorm_q8_1(x, w, None, qs, d, in_f, 1, stream=s)
+        fg.gemv_q8_0_q81(c.Wd, c.row_bytes, qs, d, y, 1, in_f, out_f, stream=s)
+        s.synchronize()
+        outs.append(host(y).tobytes())
+    assert outs[0] == outs[1]
