@@ -1,0 +1,98 @@
+"""Host-side logic of bench.py (no GPU): byte counts, copy counts, launch-shape labels, the
+rocprofv3 summarisers and the counter lookup, and the one-GPU guard."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_byte_counts_and_copies():
+    assert bench.weight_bytes("e4m3", 17408, 5120) == 89_128_960
+    assert bench.weight_bytes("q8_0", 17408, 5120) == 94_699_520
+    assert bench.grid_bytes("blk128", 17408, 5120) == 21_760
+    assert bench.grid_bytes("e4m3", 17408, 5120) == 0
+    # weights + grid + q8_1 activation (in_f + in_f/8) + f32 output
+    assert bench.algorithmic_bytes("blk128", 17408, 5120, 2) == \
+        89_128_960 + 21_760 + 2 * (5120 + 640) + 4 * 2 * 17408
+    # rotation sets exceed twice the 256 MiB last-level cache
+    for nbytes in (26_214_400, 89_128_960, 94_699_520, 4_194_304):
+        c = bench.n_copies(nbytes)
+        assert c >= 2 and c * nbytes >= 2 * bench.LLC_BYTES and (c - 1) * nbytes < 2 * bench.LLC_BYTES
+
+
+def test_launch_labels_are_unique_over_the_step():
+    sigs = {}
+    for out_f, in_f in bench.SHAPES:
+        for arm in bench.ARMS:
+            fam, grid, wg, _ = bench.launch_signature(arm, out_f, in_f)
+            key = (fam, grid, wg)
+            assert key not in sigs, (key, sigs.get(key))
+            sigs[key] = f"{arm}@{out_f}x{in_f}"
+            name = f"void fp8gemv::(anonymous namespace)::{fam}x, 1> >(int)"
+            assert bench._label_of(name, grid, wg, 0) == f"{arm}@{out_f}x{in_f}"
+
+
+def _write_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0].keys()))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_summarize_trace(tmp_path):
+    rows = []
+    for i, dur in enumerate([1000, 3000, 2000]):
+        rows.append({"Kernel_Name": "void fp8gemv::(anonymous namespace)::k_read_bytes(int)",
+                     "Grid_Size": "1024", "Workgroup_Size": "256",
+                     "Start_Timestamp": str(10_000 * i), "End_Timestamp": str(10_000 * i + dur)})
+    p = tmp_path / "trace.csv"
+    _write_csv(p, rows)
+    out = bench.summarize_trace(str(p))
+    line = [l for l in out.splitlines() if "k_read_bytes" in l][0]
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    assert cells[1] == "3"                         # calls
+    assert cells[2:6] == ["2.000", "2.000", "1.000", "3.000"]  # avg, median, min, max (us)
+
+
+def test_summarize_pmc_scales_by_the_calibration_copy(tmp_path):
+    known = bench.CALIB_MIB * 1024
+    fetch, write = [], []
+
+    def add(i, name, grid, wg, f, w):
+        base = {"Dispatch_Id": str(i), "Kernel_Name": name, "Grid_Size": str(grid),
+                "Workgroup_Size": str(wg), "LDS_Block_Size": "0"}
+        fetch.append({**base, "Counter_Name": "FETCH_SIZE", "Counter_Value": str(f)})
+        write.append({**base, "Counter_Name": "WRITE_SIZE", "Counter_Value": str(w)})
+    add(1, "__amd_rocclr_copyBuffer", 131072, 512, known / 2, known)  # FETCH reads half
+    fam, grid, wg, _ = bench.launch_signature("q8_0", 5120, 17408)
+    add(2, f"void fp8gemv::(anonymous namespace)::{fam}x> >(int)", grid, wg, 46000.0, 40.0)
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_csv(fp, fetch)
+    _write_csv(wp, write)
+    out = bench.summarize_pmc(str(fp), str(wp))
+    assert "fetch_scale 2.0000" in out and "write_scale 1.0000" in out
+    line = [l for l in out.splitlines() if "label=q8_0@5120x17408" in l][0]
+    assert int(line.rstrip(" |").split("|")[-1]) == round((46000.0 * 2 + 40.0) * 1024)
+
+
+def test_traffic_lookup_requires_the_current_source_hash(tmp_path, monkeypatch):
+    p = tmp_path / "pmc.md"
+    row = "| label=q8_0@5120x17408 | k grid=1 wg=1 | 1 | 1.0 | 1.0 | 123456 |"
+    p.write_text(f"source {bench.gemv_source_hash()}\n{row}\n")
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(p))
+    assert bench.traffic_for("q8_0@5120x17408") == 123456
+    assert bench.traffic_for("e4m3@5120x17408") is None
+    p.write_text(f"source 0000000000000000\n{row}\n")
+    assert bench.traffic_for("q8_0@5120x17408") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""

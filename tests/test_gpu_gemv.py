@@ -354,3 +354,63 @@ def test_calls_on_an_explicit_stream_are_ordered_on_it(fg):
         s.synchronize()
         outs.append(host(y).tobytes())
     assert outs[0] == outs[1]
+
+
+def _q8_0_rows(out_f, in_f, rng, scale_bits=None, q=None):
+    nb = in_f // 32
+    W = np.zeros((out_f, nb * 34), dtype=np.uint8)
+    for r in range(out_f):
+        for b in range(nb):
+            h = scale_bits(r, b) if scale_bits else 0x1400
+            W[r, 34 * b] = h & 0xFF
+            W[r, 34 * b + 1] = h >> 8
+            W[r, 34 * b + 2:34 * b + 34] = (q(r, b) if q else
+                                            rng.integers(-128, 128, 32)).astype(np.int8).view(np.uint8)
+    return W
+
+
+def test_gemv_degenerate_values(fg):
+    # The degenerate cases of the containers and the activation, against the oracle:
+    # Q8_0 quants of -128 and fp16 block scales at the largest normal, a subnormal and zero;
+    # e4m3 weights of -0.0 and +-448; activation blocks with d = 0 and with qs = +-127;
+    # a block-128 grid with zero and large tiles.
+    case("gemv degenerate values")
+    rng = np.random.default_rng(17)
+    out_f, in_f = 70, 1024  # fast paths (in_f % 256 == 0), two 1 KiB windows
+    x = synth.x_rows(in_f, 2)
+    qs, d = oracle.quantize_q8_1(x)
+    qs[0, 64:96] = 0
+    d[0, 2] = 0.0                      # a block with d = 0
+    qs[1, :32] = 127
+    qs[1, 32:64] = -127                # saturated blocks
+    d[1, 5] = 0.0
+    qsd, dd = to_dev(qs), to_dev(d)
+    scales = [0x7BFF, 0x0001, 0x0000, 0x3C00, 0x8400, 0x1400]  # 65504, 2^-24, 0, 1, -2^-14
+
+    def sb(r, b):
+        return scales[(r + b) % len(scales)]
+    Wq = _q8_0_rows(out_f, in_f, rng, scale_bits=sb,
+                    q=lambda r, b: np.full(32, -128) if (r + 2 * b) % 7 == 0 else
+                    rng.integers(-128, 128, 32))
+    y = torch.empty((2, out_f), device=dev())
+    fg.gemv_q8_0_q81(to_dev(Wq), Wq.shape[1], qsd, dd, y, 2, in_f, out_f)
+    yo, A = oracle.gemv_q8_0(Wq, Wq.shape[1], qs, d, in_f, out_f)
+    _assert_close(host(y), yo, A)
+
+    We = synth.e4m3_weights(out_f, in_f).copy()
+    We[1::5, ::7] = 0x7E                # +448
+    We[2::5, 3::7] = 0xFE               # -448
+    We[::3, :] = 0x80                   # whole rows of -0.0
+    fg.gemv_e4m3_q81(to_dev(We), in_f, 1.0, qsd, dd, y, 2, in_f, out_f)
+    yo, A = oracle.gemv_e4m3(We, in_f, 1.0, qs, d, in_f, out_f)
+    yh = host(y)
+    _assert_close(yh, yo, A)
+    assert np.all(yh[:, ::3] == 0.0)
+
+    grid = synth.blk128_grid(out_f, in_f).copy()
+    grid[0, 1] = 0.0
+    grid[0, 3] = 2.0 ** 20
+    fg.gemv_e4m3_blk128_q81(to_dev(We), in_f, to_dev(grid), grid.shape[1], qsd, dd, y, 2, in_f,
+                            out_f)
+    yo, A = oracle.gemv_e4m3_blk128(We, in_f, grid, qs, d, in_f, out_f)
+    _assert_close(host(y), yo, A)
