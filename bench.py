@@ -166,28 +166,31 @@ def cpu_baseline(shapes, arms, threads: int, reps: int = 3):
         t0 = time.perf_counter()
         wbytes = 0
         acts = {}
+        per = {}
         for arm, out_f, in_f, x, w, W, g in items:
             if (out_f, in_f) not in acts:
                 ref = oracle.rmsnorm_q8_1(x, w)
                 acts[(out_f, in_f)] = (ref["qs"], ref["d"])
             qs, d = acts[(out_f, in_f)]
             step = (out_f + nthreads - 1) // nthreads
+            tg = time.perf_counter()
             futs = [pool.submit(gemv, arm, out_f, in_f, W, g, qs, d, (r, min(out_f, r + step)))
                     for r in range(0, out_f, step)]
             for f in futs:
                 f.result()
+            per[f"{arm}@{out_f}x{in_f}"] = round((time.perf_counter() - tg) * 1e6, 1)
             wbytes += weight_bytes(arm, out_f, in_f)
-        return wbytes, time.perf_counter() - t0
+        return wbytes, time.perf_counter() - t0, per
 
-    runs = [one_step(work, threads) for _ in range(reps)]
-    wbytes = runs[0][0]
-    secs = sorted(r[1] for r in runs)[len(runs) // 2]
+    runs = sorted((one_step(work, threads) for _ in range(reps)), key=lambda r: r[1])
+    wbytes, secs, per_gemv = runs[len(runs) // 2]
     small = [it for it in work if (it[1], it[2]) == (5120, 5120)] or work[:1]
-    wb1, secs1 = one_step(small, 1)
+    wb1, secs1, per1 = one_step(small, 1)
     pool.shutdown()
     return {"value": round(wbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "ms_per_step": round(secs * 1e3, 1),
             "single_thread_GBs": round(wb1 / secs1 / 1e9, 3), "cpu_model": cpu_model(),
+            "per_gemv_us": per_gemv, "per_gemv_us_single_thread": per1,
             "sample": f"one full step (rmsnorm_q8_1 per shape + the 9 GEMVs, 3 shapes x 3 "
                       f"containers, f64 oracle, output rows split over {threads} host threads), "
                       f"median of {reps}; single_thread_GBs: the 5120x5120 part on one thread"}
