@@ -8,11 +8,13 @@
 //
 // gfx950 design (the page's kernel is a warp-per-row CUDA MMVQ doing cvt + fmaf; this one is
 // not a translation of it):
-//   * A workgroup is WAVES wave64s; each wave owns RPW consecutive weight rows.  A "window" is
-//     1024 consecutive columns: lane l streams bytes [16l, 16l+16) of the window with one
-//     16-byte non-temporal load per row, so every wave-wide load instruction reads 1 KiB of
+//   * A workgroup is WAVES wave64s; each wave owns RPW consecutive weight rows, or, with
+//     SPLIT > 1, a contiguous share of the windows of its rows (the SPLIT partial sums of a
+//     row meet in LDS and are added in part order).  A "window" is 1024 consecutive
+//     columns: lane l streams bytes [16l, 16l+16) of the window with one 16-byte
+//     non-temporal load per row, so every wave-wide load instruction reads 1 KiB of
 //     contiguous HBM and every weight byte is fetched exactly once.  U windows x RPW rows of
-//     loads are in flight per lane before any is consumed.
+//     loads are in flight per lane before any is consumed (double-buffered batches).
 //   * Order of memory operations at kernel start: first the few activation loads this thread
 //     stages, then the weight loads.  Loads of one wave complete in issue order, so staging
 //     (which waits only for the older activation loads) overlaps the weight stream instead of
@@ -20,19 +22,20 @@
 //   * The q8_1 activation row is staged once per workgroup in LDS as f16 (int8 is exact in
 //     f16, converted with the 0x6400 exponent trick; per window, the first 8 values of every
 //     lane's chunk and then the last 8, so LDS reads are contiguous across the wave) next
-//     to its block scales -- for the
-//     block-128 container the scale already times the grid value of the workgroup's
-//     128-row tile (all rows of a workgroup lie in one tile).
+//     to its block scales -- for the block-128 container the scale already times the grid
+//     value of the workgroup's 128-row tile (all rows of a workgroup lie in one tile).
 //   * Decode: v_cvt_scalef32_pk_f16_fp8 turns two e4m3 bytes into two f16 with scale 1.0
 //     (every e4m3 value, subnormals included, is exact in f16); v_dot2_f32_f16 multiplies a
 //     weight pair by an activation pair and accumulates in f32 (each product is exact: 4 + 8
 //     significant bits).  A lane's 16 columns lie in one q8_1 block and one 128-column tile,
 //     so its 16-term partial is scaled once.
-//   * At most 64 VGPRs (8 waves per SIMD): on this part occupancy, not arithmetic, decides
-//     how close the stream gets to the HBM roofline.
+//   * At most 64 VGPRs (8 waves per SIMD) for m = 1: on this part occupancy, not arithmetic,
+//     decides how close the stream gets to the HBM roofline.
 //   * Each row's 64 lane partials are summed with a DPP butterfly + fixed-order readlanes.
-// Activation rows t = blockIdx.y are independent and run identical code, so row t of an
-// m-row call is bit-identical to an m=1 call on that row.
+// Several activation rows (MT per workgroup, grid.y = ceil(m / MT)) share one weight pass:
+// each weight chunk is decoded once and multiplied into every row with the same operations
+// in the same order as for MT = 1, and every launch shape of an in_f range splits rows the
+// same way, so row t of an m-row call is bit-identical to an m=1 call on that row.
 #include "common.hpp"
 
 namespace fp8gemv {

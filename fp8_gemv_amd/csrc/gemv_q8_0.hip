@@ -34,8 +34,12 @@
 //     one or two wave-wide DPP right shifts.  A window never needs a value from the previous
 //     one, so a row can also be split between waves at any window.
 // Generic path (any in_f % 32 == 0): one lane per block, 2-byte loads; correct, not tuned.
-// Row t = blockIdx.y of the activation runs identical code, so each activation row of an
-// m-row call is bit-identical to an m=1 call on that row.
+// Several activation rows (MT per workgroup, grid.y = ceil(m / MT)) share one weight pass:
+// the scale of a weight chunk is extracted once and its dwords are split once into the parts
+// of block b0 and b0 + 1; every row's integer sums are exact, so they equal the MT = 1 prefix
+// sums, and its float operations are those of MT = 1 in the same order.  Every launch shape
+// of an in_f range splits rows the same way, so each activation row of an m-row call is
+// bit-identical to an m=1 call on that row.
 #include "common.hpp"
 
 namespace fp8gemv {
