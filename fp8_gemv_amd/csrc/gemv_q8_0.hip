@@ -399,7 +399,7 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
 }
 
 // Shapes as for the e4m3 stream: 4 waves up to in_f = 8192, 8 up to 24576, 16 beyond, with
-// double-buffered batches of 4 windows (a row of in_f = 5120 is 7 windows, the last one
+// double-buffered batches of 4, 3 and 4 windows (a row of in_f = 5120 is 7 windows, the last one
 // two groups).  In the middle range two waves share each row (4 rows per workgroup): rows of
 // 17408 columns are 23 windows, and with one wave per row a 5120-row matrix would keep only
 // 20 long-lived waves per CU, unevenly spread.
@@ -411,7 +411,7 @@ using QSmall = QCfg<4, 1, 4, 1, 2, true>;                 // in_f <= 8192, m = 1
 using QSmallB2 = QCfg<4, 1, 3, 1, 2, true, 8, 1, 2>;      //               m = 2
 using QSmallB4 = QCfg<8, 1, 2, 1, 2, true, 6, 1, 4>;      //               m = 3..4
 using QSmallB8 = QCfg<8, 2, 1, 1, 3, true, 4, 1, 8>;      //               m >= 5
-using QMid = QCfg<8, 1, 4, 2, 3, true, 8, 2>;             // in_f <= 24576, m = 1
+using QMid = QCfg<8, 1, 3, 2, 3, true, 8, 2>;             // in_f <= 24576, m = 1
 using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 2, 2>;        //                m >= 2
 using QLarge = QCfg<16, 1, 4, 2, 3, true>;                // in_f <= 65536
 static_assert(QSmall::MAX_IN_F >= 8192 && QSmallB2::MAX_IN_F >= 8192 &&
