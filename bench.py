@@ -454,11 +454,20 @@ def main() -> int:
         g = capture(lambda: [obj.launch(qs, d) for _ in range(n)])
         g.replay()
         us = timed(g.replay, n) * 1e3
+        # The pages' own protocol for comparison: host clock around launch + synchronize,
+        # median over iterations (includes launch and synchronisation latency).
+        walls = []
+        for _ in range(21):
+            t0 = time.perf_counter()
+            obj.launch(qs, d)
+            torch.cuda.synchronize()
+            walls.append((time.perf_counter() - t0) * 1e6)
         wb = weight_bytes(a, out_f, in_f)
         detail[f"{a}@{out_f}x{in_f}"] = {
             "us": round(us, 3), "weight_GBs": round(wb / us / 1e3, 1),
             "pct_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1),
-            "alg_bytes": algorithmic_bytes(a, out_f, in_f), "copies": obj.copies, "launches": n}
+            "alg_bytes": algorithmic_bytes(a, out_f, in_f), "copies": obj.copies, "launches": n,
+            "host_wall_us_median": round(sorted(walls)[len(walls) // 2], 1)}
         log(f"{a:7s} {out_f}x{in_f}: {us:8.2f} us  {wb / us / 1e3:7.1f} GB/s")
         if args.jsonl:
             with open(args.jsonl, "a") as f:
@@ -605,6 +614,14 @@ def main() -> int:
             g = capture(lambda: [run() for _ in range(50)])
             g.replay()
             prod_us[f"{variant}@{ncols}"] = round(timed(g.replay, 50) * 1e3, 3)
+            # the gate page's N = 5 host-clock launches (launch + synchronize), median
+            walls = []
+            for _ in range(5):
+                t0 = time.perf_counter()
+                run()
+                torch.cuda.synchronize()
+                walls.append((time.perf_counter() - t0) * 1e6)
+            prod_us[f"{variant}@{ncols}_host_wall_N5_median"] = round(sorted(walls)[2], 1)
 
     # SiLU-gated producer at the page's expert-ff width (fused vs two-launch chain).
     if not args.kernels_only:
