@@ -20,6 +20,7 @@ constexpr int kQuadPerm2301 = 0x4E;  // lanes {2,3,0,1} within each quad
 constexpr int kRowRor4 = 0x124;      // rotate right by 4 within each row of 16
 constexpr int kRowRor8 = 0x128;      // rotate right by 8 within each row of 16
 constexpr int kWaveShr1 = 0x138;     // shift right by one lane across the whole wave
+constexpr int kRowHalfMirror = 0x141;  // reverse lanes within each group of 8
 
 // Full row and bank masks, bound_ctrl off: every lane has a valid source for these patterns.
 template <int CTRL>

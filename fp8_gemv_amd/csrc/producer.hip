@@ -47,6 +47,21 @@ __device__ __forceinline__ void dd_add(double &hi, double &lo, double ohi, doubl
   lo = (lo + olo) + e;
 }
 
+// A double moved between lanes by DPP (both 32-bit halves with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double lane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // 1 / sqrt(mean(x^2) + eps) for one row, computed by the whole workgroup; every thread
 // returns the same value.  `red` is LDS scratch for 2 doubles per wave.
 __device__ double row_scale(const float *__restrict__ x, int ncols, float eps, double *red) {
@@ -72,17 +87,24 @@ __device__ double row_scale(const float *__restrict__ x, int ncols, float eps, d
       }
     }
   }
-  // Butterfly over the wave: both partners of a pair compute the same (commutative) result.
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const double ohi = __shfl_xor(hi, off);
-    const double olo = __shfl_xor(lo, off);
-    dd_add(hi, lo, ohi, olo);
-  }
+  // Across the wave: DPP within each row of 16 lanes (quad swaps, then rotations by 4 and
+  // 8), then the four row sums from lanes 0, 16, 32, 48 added in that fixed order.  Lanes of
+  // a row may differ in the last bits after the rotations; only the fixed lanes are read.
+  dd_add(hi, lo, dpp_f64<kQuadPerm1032>(hi), dpp_f64<kQuadPerm1032>(lo));
+  dd_add(hi, lo, dpp_f64<kQuadPerm2301>(hi), dpp_f64<kQuadPerm2301>(lo));
+  dd_add(hi, lo, dpp_f64<kRowRor4>(hi), dpp_f64<kRowRor4>(lo));
+  dd_add(hi, lo, dpp_f64<kRowRor8>(hi), dpp_f64<kRowRor8>(lo));
+  double whi = lane_f64(hi, 0), wlo = lane_f64(lo, 0);
+  double h1 = lane_f64(hi, 16), l1 = lane_f64(lo, 16);
+  double h2 = lane_f64(hi, 32), l2 = lane_f64(lo, 32);
+  double h3 = lane_f64(hi, 48), l3 = lane_f64(lo, 48);
+  dd_add(whi, wlo, h1, l1);
+  dd_add(h2, l2, h3, l3);
+  dd_add(whi, wlo, h2, l2);
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x % kWave) == 0) {
-    red[2 * wave] = hi;
-    red[2 * wave + 1] = lo;
+    red[2 * wave] = whi;
+    red[2 * wave + 1] = wlo;
   }
   __syncthreads();
   double thi = red[0], tlo = red[1];
@@ -108,9 +130,10 @@ __device__ __forceinline__ float h_value(float g, float u) {
 // scale is returned through d_out (same value on all 8 lanes).
 __device__ __forceinline__ uint32_t quant_group(const float z[4], float &d_out) {
   float amax = fmaxf(fmaxf(fabsf(z[0]), fabsf(z[1])), fmaxf(fabsf(z[2]), fabsf(z[3])));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  // max over the 8 lanes (exact in any order): quad swaps, then the mirror within 8 lanes
+  amax = fmaxf(amax, dpp_f32<kQuadPerm1032>(amax));
+  amax = fmaxf(amax, dpp_f32<kQuadPerm2301>(amax));
+  amax = fmaxf(amax, dpp_f32<kRowHalfMirror>(amax));
   const float d = amax / 127.0f;
   const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
   uint32_t packed = 0;
