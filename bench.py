@@ -73,6 +73,31 @@ def n_copies(nbytes: int) -> int:
     return max(2, math.ceil(2 * LLC_BYTES / nbytes))
 
 
+def fit_read_ceiling(points):
+    """Least-squares fit of t = fixed + bytes / steady over (bytes, us) points of one read kernel.
+
+    Returns the steady stream rate, the fixed cost per launch, and the fixed cost that would
+    still allow 85% of peak at each measured size (negative: not reachable at that size).
+    """
+    n = len(points)
+    if n < 2:
+        raise ValueError("need at least two sizes")
+    xs = [float(b) for b, _ in points]
+    ys = [float(t) for _, t in points]
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    if sxx == 0:
+        raise ValueError("need two different sizes")
+    slope = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx  # us per byte
+    fixed = my - slope * mx
+    steady = 1.0 / slope / 1e3  # GB/s
+    budget = {f"{b / 1e6:.1f}MB": round(b / (0.85 * HBM_PEAK_GBS * 1e3) - b / (steady * 1e3), 3)
+              for b, _ in points}
+    return {"points": [{"bytes": int(b), "us": t} for b, t in points],
+            "steady_GBs": round(steady, 1), "steady_pct_peak": round(100 * steady / HBM_PEAK_GBS, 1),
+            "fixed_us": round(fixed, 3), "fixed_budget_for_85pct_us": budget}
+
+
 class Arm:
     """Rotated device copies of one container at one shape, plus its launch."""
 
@@ -123,8 +148,14 @@ def cpu_model() -> str:
 
 
 def gpu_state() -> dict:
-    """Current clocks and temperatures of the GPU, from rocm-smi run as a child process."""
+    """Current clocks and temperatures of the GPU, from rocm-smi run as a child process.
+
+    Skipped under rocprofv3: its preloaded library would start the GPU in the child before
+    rocm-smi's launcher replaces itself with the Python interpreter.
+    """
     import subprocess
+    if any(k.startswith("ROCPROF_") for k in os.environ):
+        return {"skipped": "running under rocprofv3"}
     try:
         out = subprocess.run(["rocm-smi", "--showtemp", "-c", "--json"], capture_output=True,
                              text=True, timeout=30).stdout
@@ -595,6 +626,30 @@ def main() -> int:
         if shape in ceiling:
             v["pct_of_read_ceiling"] = round(100 * (v["weight_GBs"] / ceiling[shape]["GBs"]), 1)
 
+    # The read ceiling as a function of size: the same kernel over 2x and 4x the 89 MB plane,
+    # cold by rotation, fitted as t = fixed + bytes / steady.  The fit says how much of the gap
+    # to peak is a per-launch cost and how much is the stream rate itself.
+    read_fit = None
+    if not args.kernels_only and ceiling:
+        pts = [(v["bytes"], v["us"]) for v in ceiling.values()]
+        for mult in (2, 4):
+            nbytes = mult * weight_bytes("e4m3", 17408, 5120)
+            copies = n_copies(nbytes)
+            bufs = [torch.full((nbytes,), 0x11, dtype=torch.uint8, device=dev)
+                    for _ in range(copies)]
+            n = max(args.kernel_iters // 2, copies)
+            g = capture(lambda: [fg.fp8gemv_read_bytes(bufs[i % copies], nbytes, sink)
+                                 for i in range(n)])
+            g.replay()
+            us = timed(g.replay, n) * 1e3
+            pts.append((nbytes, round(us, 3)))
+            log(f"read    {nbytes / 1e6:7.1f} MB: {us:8.2f} us  {nbytes / us / 1e3:7.1f} GB/s")
+            del g, bufs
+            torch.cuda.empty_cache()
+        read_fit = fit_read_ceiling(pts)
+        log(f"read fit: steady {read_fit['steady_GBs']} GB/s ({read_fit['steady_pct_peak']}%), "
+            f"fixed {read_fit['fixed_us']} us per launch")
+
     # Producer alone (latency-bound; the gate page's site widths), fused vs two-launch chain.
     prod_us = {}
     for ncols in (() if args.kernels_only else (1536, 4096, 8192)):
@@ -716,7 +771,7 @@ def main() -> int:
                    "eps": EPS, "e4m3_scale": SCALE},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
-        "gemv": detail, "read_ceiling": ceiling, "m_rows": m_rows, "sheets": sheets,
+        "gemv": detail, "read_ceiling": ceiling, "read_fit": read_fit, "m_rows": m_rows, "sheets": sheets,
         "requant": requant,
         "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu, "cold_check": cold,

@@ -96,3 +96,20 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_read_ceiling_fit_recovers_a_line():
+    # t = 1.5 us + bytes / 7000 GB/s, sampled at four sizes: the fit must return both exactly.
+    pts = [(b, 1.5 + b / 7000e3) for b in (26214400, 89128960, 178257920, 356515840)]
+    fit = bench.fit_read_ceiling(pts)
+    assert fit["steady_GBs"] == pytest.approx(7000.0, abs=0.05)
+    assert fit["fixed_us"] == pytest.approx(1.5, abs=5e-4)
+    assert fit["steady_pct_peak"] == pytest.approx(87.5, abs=0.05)
+    # fixed cost allowed at 89 MB for 85% of 8 TB/s at a 7 TB/s stream
+    b = 89128960
+    assert fit["fixed_budget_for_85pct_us"]["89.1MB"] == pytest.approx(
+        b / 6800e3 - b / 7000e3, abs=1e-3)
+    with pytest.raises(ValueError):
+        bench.fit_read_ceiling(pts[:1])
+    with pytest.raises(ValueError):
+        bench.fit_read_ceiling([pts[0], pts[0]])
