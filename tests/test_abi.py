@@ -179,3 +179,17 @@ def test_byte_counts_match_the_pages(fg):
     g = fg.blk128_grid_bytes(17408, 5120)
     assert g == 21760 and g == fg.blk128_grid_bytes(5120, 17408)
     assert round(100 * g / fg.e4m3_weight_bytes(17408, 5120), 2) == 0.02
+
+
+def test_public_header_is_plain_c():
+    # the C consumer of the ABI (a GPU test runs it) must compile as C11 against the header
+    import shutil
+    import subprocess
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import c_abi_build
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not on PATH")
+    r = subprocess.run(c_abi_build.compile_cmd("", syntax_only=True), capture_output=True,
+                       text=True)
+    assert r.returncode == 0, r.stderr
