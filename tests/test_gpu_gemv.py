@@ -218,6 +218,22 @@ def test_max_in_f(fg, kind):
     _assert_close(y, yo, A)
 
 
+# The largest m the library accepts (the launch grid's y dimension indexes activation rows):
+# in_f = 256 takes the Q8_0 fast path, and m = 65535 is 8192 passes of 8 rows, the last one
+# with a single row.  Every output against the oracle, and sampled rows bit-identical to m=1.
+@pytest.mark.parametrize("kind", KINDS)
+def test_max_m(fg, kind):
+    m, out_f, in_f = 65535, 5, 256
+    case(f"{kind} m={m} out_f={out_f} in_f={in_f}")
+    c = Case(kind, out_f, in_f, m)
+    y = c.gpu(fg)
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+    for t in (0, 1, 7, 8, 32767, m - 2, m - 1):
+        y1 = c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)
+        assert y1[0].tobytes() == y[t].tobytes(), f"row {t}"
+
+
 def test_bad_arguments_raise_and_launch_nothing(fg):
     case("argument errors through the binding")
     c = Case("e4m3", 64, 256, 1)

@@ -62,6 +62,20 @@ def test_rmsnorm_q8_1_matches_oracle(fg, ncols, nrows):
     assert np.array_equal(qs, ref["qs"]) and np.array_equal(d, ref["d"])
 
 
+def test_max_nrows(fg):
+    # the largest row count the library accepts (the launch grid's y dimension indexes rows)
+    nrows, ncols = 65535, 64
+    case(f"rmsnorm_q8_1 ncols={ncols} nrows={nrows}")
+    x = synth.x_rows(ncols, nrows)
+    w = synth.gain(ncols)
+    z, qs, d = _gpu_producer(fg, x, w)
+    ref = oracle.rmsnorm_q8_1(x, w)
+    assert np.array_equal(z.view(np.uint32), ref["z32"].view(np.uint32))
+    assert np.array_equal(qs, ref["qs"]) and np.array_equal(d, ref["d"])
+    zc, qc, dc = _gpu_chain(fg, x, w)
+    assert zc.tobytes() == z.tobytes() and qc.tobytes() == qs.tobytes() and dc.tobytes() == d.tobytes()
+
+
 @pytest.mark.parametrize("nrows", [1, 2])
 @pytest.mark.parametrize("ncols", [1536, 4096, 8192, 32, 5120, 17408])
 def test_fused_is_byte_identical_to_chain(fg, ncols, nrows):
