@@ -100,6 +100,18 @@ def _stream(stream, dev=None) -> int:
     return int(stream)
 
 
+def _run(name: str, dev, *args) -> None:
+    """Call one entry point with the tensors' device current: the library launches on the
+    current HIP device and raises per-device kernel attributes there."""
+    fn = getattr(_lib, name)
+    if dev is None:
+        rc = fn(*args)
+    else:
+        with torch.cuda.device(dev):
+            rc = fn(*args)
+    _check(name, rc)
+
+
 def _ptr(t, name: str, dtype, min_numel: int, device=None):
     if t is None:
         return None
@@ -127,62 +139,63 @@ def _dev(t):
 def rms_norm_f32(x, w, z, ncols: int, nrows: int, eps: float = 1e-6, stream=None) -> None:
     """z[r, :] = x[r, :] * w / sqrt(mean(x[r, :]^2) + eps)  (first half of the chain)."""
     dev = _dev(x)
-    rc = _lib.rms_norm_f32(_ptr(x, "x", torch.float32, ncols * nrows, dev),
-                           _ptr(w, "w", torch.float32, ncols, dev),
-                           _ptr(z, "z", torch.float32, ncols * nrows, dev),
-                           ncols, nrows, eps, _stream(stream, dev))
-    _check("rms_norm_f32", rc)
+    _run("rms_norm_f32", dev,
+         _ptr(x, "x", torch.float32, ncols * nrows, dev),
+         _ptr(w, "w", torch.float32, ncols, dev),
+         _ptr(z, "z", torch.float32, ncols * nrows, dev),
+         ncols, nrows, eps, _stream(stream, dev))
 
 
 def quantize_q8_1(z, qs, d, nrows: int, ncols: int, stream=None) -> None:
     """q8_1 of f32 rows: qs int8 [nrows, ncols], d f32 [nrows, ncols/32]."""
     dev = _dev(z)
-    rc = _lib.quantize_q8_1(_ptr(z, "z", torch.float32, ncols * nrows, dev),
-                            _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
-                            _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
-                            nrows, ncols, _stream(stream, dev))
-    _check("quantize_q8_1", rc)
+    _run("quantize_q8_1", dev,
+         _ptr(z, "z", torch.float32, ncols * nrows, dev),
+         _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
+         _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
+         nrows, ncols, _stream(stream, dev))
 
 
 def rmsnorm_q8_1(x, w, z, qs, d, ncols: int, nrows: int, eps: float = 1e-6,
                  stream=None) -> None:
     """Fused producer: RMSNorm then q8_1 in one launch (z may be None)."""
     dev = _dev(x)
-    rc = _lib.rmsnorm_q8_1(_ptr(x, "x", torch.float32, ncols * nrows, dev),
-                           _ptr(w, "w", torch.float32, ncols, dev),
-                           _ptr(z, "z", torch.float32, ncols * nrows, dev),
-                           _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
-                           _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
-                           ncols, nrows, eps, _stream(stream, dev))
-    _check("rmsnorm_q8_1", rc)
+    _run("rmsnorm_q8_1", dev,
+         _ptr(x, "x", torch.float32, ncols * nrows, dev),
+         _ptr(w, "w", torch.float32, ncols, dev),
+         _ptr(z, "z", torch.float32, ncols * nrows, dev),
+         _ptr(qs, "qs", torch.int8, ncols * nrows, dev),
+         _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
+         ncols, nrows, eps, _stream(stream, dev))
 
 
 def silu_mul_f32(gate, up, h, ncols: int, nrows: int, stream=None) -> None:
     """h = silu(gate) * up (first half of the SiLU-gated chain)."""
     dev = _dev(gate)
     n = ncols * nrows
-    rc = _lib.silu_mul_f32(_ptr(gate, "gate", torch.float32, n, dev),
-                           _ptr(up, "up", torch.float32, n, dev),
-                           _ptr(h, "h", torch.float32, n, dev), ncols, nrows, _stream(stream, dev))
-    _check("silu_mul_f32", rc)
+    _run("silu_mul_f32", dev,
+         _ptr(gate, "gate", torch.float32, n, dev),
+         _ptr(up, "up", torch.float32, n, dev),
+         _ptr(h, "h", torch.float32, n, dev),
+         ncols, nrows, _stream(stream, dev))
 
 
 def silu_mul_q8_1(gate, up, h, qs, d, ncols: int, nrows: int, stream=None) -> None:
     """Fused SiLU-gated producer: silu(gate) * up then q8_1 in one launch (h may be None)."""
     dev = _dev(gate)
     n = ncols * nrows
-    rc = _lib.silu_mul_q8_1(_ptr(gate, "gate", torch.float32, n, dev),
-                            _ptr(up, "up", torch.float32, n, dev),
-                            _ptr(h, "h", torch.float32, n, dev),
-                            _ptr(qs, "qs", torch.int8, n, dev),
-                            _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
-                            ncols, nrows, _stream(stream, dev))
-    _check("silu_mul_q8_1", rc)
+    _run("silu_mul_q8_1", dev,
+         _ptr(gate, "gate", torch.float32, n, dev),
+         _ptr(up, "up", torch.float32, n, dev),
+         _ptr(h, "h", torch.float32, n, dev),
+         _ptr(qs, "qs", torch.int8, n, dev),
+         _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
+         ncols, nrows, _stream(stream, dev))
 
 
 # -------------------------------------------------------------------------------- GEMVs
 
-def _w_numel(row_bytes: int, out_f: int, in_f: int, container_row: int) -> int:
+def _w_numel(row_bytes: int, out_f: int, container_row: int) -> int:
     # the last row only needs its used bytes
     return (out_f - 1) * row_bytes + container_row if out_f >= 1 else 0
 
@@ -191,42 +204,37 @@ def gemv_q8_0_q81(W, row_bytes: int, qs, d, y, m: int, in_f: int, out_f: int,
                   stream=None) -> None:
     """y[m, out_f] = Q8_0 weight rows W times the q8_1 activation (qs, d)."""
     dev = _dev(W)
-    rc = _lib.gemv_q8_0_q81(_ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f,
-                                                                in_f // 32 * 34), dev),
-                            row_bytes,
-                            _ptr(qs, "qs", torch.int8, m * in_f, dev),
-                            _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
-                            _ptr(y, "y", torch.float32, m * out_f, dev),
-                            m, in_f, out_f, _stream(stream, dev))
-    _check("gemv_q8_0_q81", rc)
+    _run("gemv_q8_0_q81", dev,
+         _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f // 32 * 34), dev), row_bytes,
+         _ptr(qs, "qs", torch.int8, m * in_f, dev),
+         _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
+         _ptr(y, "y", torch.float32, m * out_f, dev),
+         m, in_f, out_f, _stream(stream, dev))
 
 
 def gemv_e4m3_q81(W, row_bytes: int, scale: float, qs, d, y, m: int, in_f: int, out_f: int,
                   stream=None) -> None:
     """y[m, out_f] = scale * e4m3 weights W times the q8_1 activation (qs, d)."""
     dev = _dev(W)
-    rc = _lib.gemv_e4m3_q81(_ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f),
-                                 dev),
-                            row_bytes, scale,
-                            _ptr(qs, "qs", torch.int8, m * in_f, dev),
-                            _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
-                            _ptr(y, "y", torch.float32, m * out_f, dev),
-                            m, in_f, out_f, _stream(stream, dev))
-    _check("gemv_e4m3_q81", rc)
+    _run("gemv_e4m3_q81", dev,
+         _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f), dev), row_bytes, scale,
+         _ptr(qs, "qs", torch.int8, m * in_f, dev),
+         _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
+         _ptr(y, "y", torch.float32, m * out_f, dev),
+         m, in_f, out_f, _stream(stream, dev))
 
 
 def gemv_e4m3_blk128_q81(W, row_bytes: int, grid, grid_cols: int, qs, d, y, m: int, in_f: int,
                          out_f: int, stream=None) -> None:
     """y[m, out_f] = block-128-scaled e4m3 weights W times the q8_1 activation (qs, d)."""
     dev = _dev(W)
-    rc = _lib.gemv_e4m3_blk128_q81(
-        _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f), dev), row_bytes,
-        _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
-        _ptr(qs, "qs", torch.int8, m * in_f, dev),
-        _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
-        _ptr(y, "y", torch.float32, m * out_f, dev),
-        m, in_f, out_f, _stream(stream, dev))
-    _check("gemv_e4m3_blk128_q81", rc)
+    _run("gemv_e4m3_blk128_q81", dev,
+         _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f), dev), row_bytes,
+         _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
+         _ptr(qs, "qs", torch.int8, m * in_f, dev),
+         _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
+         _ptr(y, "y", torch.float32, m * out_f, dev),
+         m, in_f, out_f, _stream(stream, dev))
 
 
 # --------------------------------------------------------------------------- requantiser
@@ -239,31 +247,29 @@ def requant_e4m3_q8_0(W, row_bytes: int, scale: float, Wq, q_row_bytes: int, in_
                       out_f: int, stream=None) -> None:
     """Load-time e4m3 (per-tensor scale) -> Q8_0 rows in Wq (uint8)."""
     dev = _dev(W)
-    rc = _lib.requant_e4m3_q8_0(_ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f),
-                                     dev), row_bytes, scale,
-                                _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev),
-                                q_row_bytes, in_f, out_f, _stream(stream, dev))
-    _check("requant_e4m3_q8_0", rc)
+    _run("requant_e4m3_q8_0", dev,
+         _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f), dev), row_bytes, scale,
+         _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev), q_row_bytes,
+         in_f, out_f, _stream(stream, dev))
 
 
 def requant_e4m3_blk128_q8_0(W, row_bytes: int, grid, grid_cols: int, Wq, q_row_bytes: int,
                              in_f: int, out_f: int, stream=None) -> None:
     """Load-time block-128 e4m3 -> Q8_0 rows in Wq (uint8)."""
     dev = _dev(W)
-    rc = _lib.requant_e4m3_blk128_q8_0(
-        _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f, in_f), dev), row_bytes,
-        _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
-        _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev), q_row_bytes,
-        in_f, out_f, _stream(stream, dev))
-    _check("requant_e4m3_blk128_q8_0", rc)
+    _run("requant_e4m3_blk128_q8_0", dev,
+         _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f), dev), row_bytes,
+         _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
+         _ptr(Wq, "Wq", torch.uint8, _q_numel(q_row_bytes, out_f, in_f), dev), q_row_bytes,
+         in_f, out_f, _stream(stream, dev))
 
 
 def fp8gemv_read_bytes(buf, nbytes: int, sink, stream=None) -> None:
     """Measurement aid: stream nbytes of buf with the GEMVs' load pattern (no result)."""
     dev = _dev(buf)
-    rc = _lib.fp8gemv_read_bytes(_ptr(buf, "buf", torch.uint8, nbytes, dev), nbytes,
-                                 _ptr(sink, "sink", torch.int32, 1, dev), _stream(stream, dev))
-    _check("fp8gemv_read_bytes", rc)
+    _run("fp8gemv_read_bytes", dev,
+         _ptr(buf, "buf", torch.uint8, nbytes, dev), nbytes,
+         _ptr(sink, "sink", torch.int32, 1, dev), _stream(stream, dev))
 
 
 # ------------------------------------------------------------------------- byte counts
