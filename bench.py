@@ -332,6 +332,72 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
     return "\n".join(lines)
 
 
+CU_NUM = 256  # MI355X compute units
+
+
+SCLK_GHZ = 2.4  # MI355X peak engine clock (rocm-smi reads 2402 MHz under this load)
+
+
+def summarize_sq(csv_paths) -> str:
+    """Median per-dispatch SQ counters per kernel launch shape over one or more rocprofv3 --pmc
+    passes, and what they imply for one dispatch of the given duration (its own timestamps):
+
+      VALU % = VALU instructions x 4 cycles / SIMDs / (duration x SCLK_GHZ): the share of
+               SIMD time spent issuing VALU work (a wave64 VALU instruction holds its SIMD for
+               one quad-cycle; SQ_ACTIVE_INST_VALU counts exactly the instructions);
+      LDS %  = the same for the quad-cycles of LDS instructions (SQ_ACTIVE_INST_LDS);
+      occupancy % = SQ_WAVE_CYCLES (quad-cycles) x 4 / (duration x SCLK_GHZ) / (CUs x 32);
+      LDS wait % / any wait % = SQ_WAIT_INST_LDS, SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES;
+      instructions per wave; LDS bank conflicts per conflict-free LDS cycle.
+    """
+    import csv
+    import statistics
+    vals, durs = {}, {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            key = _kernel_key(r["Kernel_Name"], r["Grid_Size"], r["Workgroup_Size"])
+            d = (path, r["Dispatch_Id"])
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], {})[d] = float(r["Counter_Value"])
+            durs.setdefault(key, {})[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    med = {k: {c: statistics.median(v.values()) for c, v in cs.items()} for k, cs in vals.items()}
+    dur = {k: statistics.median(v.values()) for k, v in durs.items()}  # ns
+    simds = CU_NUM * 4
+    keep = [k for k in sorted(med) if "gemv" in k or "rmsnorm" in k]
+
+    def cycles(k):
+        return dur[k] * SCLK_GHZ
+
+    derived = [
+        ("us", lambda k, c: dur[k] / 1e3),
+        ("VALU %", lambda k, c: 100 * c["SQ_INSTS_VALU"] * 4 / simds / cycles(k)),
+        ("LDS %", lambda k, c: 100 * c["SQ_ACTIVE_INST_LDS"] * 4 / simds / cycles(k)),
+        ("occupancy %", lambda k, c: 100 * c["SQ_WAVE_CYCLES"] * 4 / cycles(k) / (CU_NUM * 32)),
+        ("LDS wait %", lambda k, c: 100 * c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]),
+        ("any wait %", lambda k, c: 100 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+        ("VALU inst / wave", lambda k, c: c["SQ_INSTS_VALU"] / c["SQ_WAVES"]),
+        ("LDS inst / wave", lambda k, c: c["SQ_INSTS_LDS"] / c["SQ_WAVES"]),
+        ("bank conflicts", lambda k, c: c["SQ_LDS_BANK_CONFLICT"]
+         / max(c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"], 1.0)),
+    ]
+    counters = sorted({c for k in keep for c in med[k]})
+    lines = ["| kernel (grid = threads) | " + " | ".join(n for n, _ in derived) + " |",
+             "|---" * (len(derived) + 1) + "|"]
+    for k in keep:
+        cells = []
+        for _, f in derived:
+            try:
+                cells.append(f"{f(k, med[k]):.2f}")
+            except (KeyError, ZeroDivisionError):
+                cells.append("-")
+        lines.append(f"| {k} | " + " | ".join(cells) + " |")
+    lines += ["", "Raw medians per dispatch:", "",
+              "| kernel | " + " | ".join(counters) + " |", "|---" * (len(counters) + 1) + "|"]
+    for k in keep:
+        lines.append(f"| {k} | " + " | ".join(
+            f"{med[k][c]:.0f}" if c in med[k] else "-" for c in counters) + " |")
+    return "\n".join(lines)
+
+
 def traffic_for(kernel_label: str):
     """HBM bytes per launch of a GEMV from the committed counter summary, or None when the
     summary is missing, does not cover this launch, or was taken on other kernel sources."""
@@ -364,6 +430,11 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run 4 device-to-device copies of this many MiB (a plain copy "
                          "kernel of known size that calibrates the HBM byte counters)")
+    ap.add_argument("--m-rows-only", action="store_true",
+                    help="run only the small-batch (m rows) timing and print its JSON (short "
+                         "runs under a profiler); needs 17408x5120 among --shapes")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="COUNTER_CSV",
+                    help="print a markdown summary of rocprofv3 SQ/GRBM counter passes, exit")
     ap.add_argument("--no-sheets", action="store_true",
                     help="skip the 27B / 1.7B projection shape sheets")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
@@ -374,6 +445,9 @@ def main() -> int:
 
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_sq:
+        print(summarize_sq(args.summarize_sq))
         return 0
     if args.summarize_pmc:
         print(f"source {gemv_source_hash()}")
@@ -442,6 +516,41 @@ def main() -> int:
         torch.cuda.synchronize()
         return g
 
+    def run_m_rows():
+        """Small-batch rows (gemv_e4m3_bench.rs: m in {1, 2, 4, 8} through grid.y at
+        17408x5120): m activation rows from the producer with nrows = m, one GEMV call per
+        launch, weights counted once per call."""
+        out = {}
+        out_f, in_f = SHAPE_M
+        xm = torch.from_numpy(synth.x_rows(in_f, MAX_M)).to(dev)
+        wm = torch.from_numpy(synth.gain(in_f)).to(dev)
+        qsm = torch.empty(MAX_M * in_f, dtype=torch.int8, device=dev)
+        dm = torch.empty(MAX_M * (in_f // 32), device=dev)
+        fg.rmsnorm_q8_1(xm, wm, None, qsm, dm, in_f, MAX_M, EPS)
+        for a in arms:
+            obj = arm_objs[(out_f, in_f, a)]
+            for m in M_ROWS:
+                n = max(args.kernel_iters, obj.copies)
+                g = capture(lambda: [obj.launch(qsm, dm, m) for _ in range(n)])
+                g.replay()
+                us = timed(g.replay, n) * 1e3
+                wb = weight_bytes(a, out_f, in_f)
+                out[f"{a}@{out_f}x{in_f}@m={m}"] = {
+                    "us": round(us, 3), "us_per_row": round(us / m, 3),
+                    "weight_GBs": round(wb / us / 1e3, 1),
+                    "alg_bytes": algorithmic_bytes(a, out_f, in_f, m)}
+                log(f"{a:7s} {out_f}x{in_f} m={m}: {us:8.2f} us  {us / m:7.2f} us/row")
+        return out
+
+    if args.m_rows_only:
+        # a short run of the small-batch section alone (for counter collection); prints its
+        # own JSON line, not the bench line
+        if SHAPE_M not in shapes:
+            log(f"--m-rows-only needs --shapes to include {SHAPE_M[0]}x{SHAPE_M[1]}")
+            return 2
+        print(json.dumps({"m_rows": run_m_rows()}), flush=True)
+        return 0
+
     if args.copy_mib:
         nbytes = args.copy_mib << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
@@ -505,30 +614,7 @@ def main() -> int:
                 f.write(json.dumps({"arm": a, "out_f": out_f, "in_f": in_f,
                                     **detail[f"{a}@{out_f}x{in_f}"]}) + "\n")
 
-    # Small-batch rows (gemv_e4m3_bench.rs: m in {1, 2, 4, 8} through grid.y at 17408x5120):
-    # m activation rows from the producer with nrows = m, one GEMV call per launch, weights
-    # counted once per call.
-    m_rows = {}
-    if SHAPE_M in shapes and not args.kernels_only:
-        out_f, in_f = SHAPE_M
-        xm = torch.from_numpy(synth.x_rows(in_f, MAX_M)).to(dev)
-        wm = torch.from_numpy(synth.gain(in_f)).to(dev)
-        qsm = torch.empty(MAX_M * in_f, dtype=torch.int8, device=dev)
-        dm = torch.empty(MAX_M * (in_f // 32), device=dev)
-        fg.rmsnorm_q8_1(xm, wm, None, qsm, dm, in_f, MAX_M, EPS)
-        for a in arms:
-            obj = arm_objs[(out_f, in_f, a)]
-            for m in M_ROWS:
-                n = max(args.kernel_iters, obj.copies)
-                g = capture(lambda: [obj.launch(qsm, dm, m) for _ in range(n)])
-                g.replay()
-                us = timed(g.replay, n) * 1e3
-                wb = weight_bytes(a, out_f, in_f)
-                m_rows[f"{a}@{out_f}x{in_f}@m={m}"] = {
-                    "us": round(us, 3), "us_per_row": round(us / m, 3),
-                    "weight_GBs": round(wb / us / 1e3, 1),
-                    "alg_bytes": algorithmic_bytes(a, out_f, in_f, m)}
-                log(f"{a:7s} {out_f}x{in_f} m={m}: {us:8.2f} us  {us / m:7.2f} us/row")
+    m_rows = run_m_rows() if SHAPE_M in shapes and not args.kernels_only else {}
 
     # Projection shape sheets (gemv_e4m3_bench.rs, main: the 27B and 1.7B sheets, the three
     # arms per shape on their own rotated copies, ratio = t_q8_0 / t_e4m3, ratio_blk =
