@@ -113,3 +113,28 @@ def test_read_ceiling_fit_recovers_a_line():
         bench.fit_read_ceiling(pts[:1])
     with pytest.raises(ValueError):
         bench.fit_read_ceiling([pts[0], pts[0]])
+
+
+def test_summarize_sq_derives_shares_from_counters_and_duration(tmp_path):
+    # one dispatch of 10 us at 2.4 GHz = 24000 cycles; 1024 SIMDs
+    dur_ns = 10_000
+    name = "void fp8gemv::(anonymous namespace)::k_gemv_e4m3<false, Cfg<4> >(int)"
+    counters = {
+        "SQ_INSTS_VALU": 0.5 * 24000 / 4 * 1024,      # half the SIMD time in VALU
+        "SQ_ACTIVE_INST_LDS": 0.1 * 24000 / 4 * 1024,  # a tenth in LDS instructions
+        "SQ_WAVE_CYCLES": 0.25 * 24000 / 4 * 256 * 32,  # a quarter of the wave slots
+        "SQ_WAIT_INST_LDS": 0.02 * 0.25 * 24000 / 4 * 256 * 32,
+        "SQ_WAIT_INST_ANY": 0.3 * 0.25 * 24000 / 4 * 256 * 32,
+        "SQ_WAVES": 1000.0, "SQ_INSTS_LDS": 20000.0,
+        "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 110.0,
+    }
+    rows = [{"Dispatch_Id": "7", "Kernel_Name": name, "Grid_Size": "1024", "Workgroup_Size": "256",
+             "Counter_Name": c, "Counter_Value": str(v), "Start_Timestamp": "1000",
+             "End_Timestamp": str(1000 + dur_ns)} for c, v in counters.items()]
+    p = tmp_path / "sq.csv"
+    _write_csv(p, rows)
+    out = bench.summarize_sq([str(p)])
+    line = [l for l in out.splitlines() if "k_gemv_e4m3" in l and "grid=1024" in l][0]
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    assert cells[1:] == ["10.00", "50.00", "10.00", "25.00", "2.00", "30.00", "3072.00",
+                         "20.00", "0.10"]
