@@ -37,7 +37,10 @@
 // Several activation rows (MT per workgroup, grid.y = ceil(m / MT)) share one weight pass:
 // the scale of a weight chunk is extracted once and its dwords are split once into the parts
 // of block b0 and b0 + 1; every row's integer sums are exact, so they equal the MT = 1 prefix
-// sums, and its float operations are those of MT = 1 in the same order.  Every launch shape
+// sums, and its float operations are those of MT = 1 in the same order.  (With MT > 1 the
+// fp16 scale of a chunk's first block is moved between lanes once per window and each row
+// multiplies it by its own d_a there; that is the product the scale's own lane forms for
+// MT = 1, so the bits are the same.)  Every launch shape
 // of an in_f range splits rows the same way, so each activation row of an m-row call is
 // bit-identical to an m=1 call on that row.
 #include "common.hpp"
@@ -219,6 +222,7 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   // the scale of b0 sits delta = 0, 1 or 2 lanes to the left
   const bool d0 = o == 0, d1 = o != 0 && o <= 16;
   const int dsc_lane = 8 * gidx + (has_scale ? hb : 0);  // d_a entry of the scale, per window + 24
+  const int dsc_b0 = 8 * gidx + b0;                       // d_a entry of the chunk's first block
   const int lds_lane = lane < kWinLanes ? lane * 16 : 0;  // lanes 51..63 multiply zero weights
   __syncthreads();
 
@@ -249,23 +253,39 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
       }
       // Activation row tt's chunk and scale from LDS; row tt + 1 is read while row tt is
       // multiplied, so the LDS latency is not paid once per row.
-      auto read_row = [&](int tt, int4_t &a, float &da) {
+      auto read_row = [&](int tt, int4_t &a, float &da, float &da0) {
         const unsigned char *arow = lds + tt * row_lds;
         a = *reinterpret_cast<const int4_t *>(arow + win * kWinBytes + lds_lane);
-        da = reinterpret_cast<const float *>(arow + nwin * kWinBytes)[win * kWinBlocks + dsc_lane];
+        const float *dsc = reinterpret_cast<const float *>(arow + nwin * kWinBytes) + win * kWinBlocks;
+        da = dsc[dsc_lane];
+        if constexpr (MT > 1) da0 = dsc[dsc_b0];
       };
+      // MT > 1: the fp16 scale of the chunk's first block is fetched from its lane once per
+      // window; each row then forms the same product (scale x d_a of that block) locally.
+      float hw0[RPW];
+      if constexpr (MT > 1) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const float g1 = wave_shr1(hw[r]);
+          const float g2 = wave_shr1(g1);
+          hw0[r] = d0 ? hw[r] : (d1 ? g1 : g2);
+        }
+      }
       int4_t abuf[2];
-      float dbuf[2];
-      read_row(0, abuf[0], dbuf[0]);
+      float dbuf[2], d0buf[2];
+      read_row(0, abuf[0], dbuf[0], d0buf[0]);
 #pragma unroll
       for (int tt = 0; tt < MT; ++tt) {
-        if (tt + 1 < MT) read_row(tt + 1, abuf[(tt + 1) & 1], dbuf[(tt + 1) & 1]);
+        if (tt + 1 < MT) read_row(tt + 1, abuf[(tt + 1) & 1], dbuf[(tt + 1) & 1], d0buf[(tt + 1) & 1]);
         const int4_t a = abuf[tt & 1];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
           const float H = hw[r] * dbuf[tt & 1];
-          const float h1 = wave_shr1(H);   // scale of chunk c - 1
-          const float h2 = wave_shr1(h1);  // scale of chunk c - 2
+          float h1 = 0.0f, h2 = 0.0f;
+          if constexpr (MT == 1) {
+            h1 = wave_shr1(H);   // scale of chunk c - 1
+            h2 = wave_shr1(h1);  // scale of chunk c - 2
+          }
           int s_lo, s_hi;
           if constexpr (MT == 1) {
             const int4_t w = wb[u][r];
@@ -284,7 +304,12 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
             s_hi = __builtin_amdgcn_sdot4(whi[r][2], a[2], s_hi, false);
             s_hi = __builtin_amdgcn_sdot4(whi[r][3], a[3], s_hi, false);
           }
-          const float S0 = d0 ? H : (d1 ? h1 : h2);
+          float S0;
+          if constexpr (MT == 1) {
+            S0 = d0 ? H : (d1 ? h1 : h2);
+          } else {
+            S0 = hw0[r] * d0buf[tt & 1];
+          }
           acc[tt][r] = fmaf((float)s_lo, S0, acc[tt][r]);
           acc[tt][r] = fmaf((float)s_hi, H, acc[tt][r]);
         }
