@@ -253,27 +253,38 @@ def _kernel_key(name: str, grid: str, wg: str) -> str:
 
 
 def launch_signature(arm: str, out_f: int, in_f: int):
-    """(kernel family, grid threads, workgroup size, LDS bytes) of the library's launch for
-    one GEMV -- the launch-shape choice of the HIP library restated for labelling profiles."""
-    waves = 4 if in_f <= 8192 else (8 if in_f <= 24576 else 16)
-    split = 2 if 8192 < in_f <= 24576 else 1  # waves sharing a row in the middle range
+    """(kernel family, launch configuration, grid threads, workgroup size, LDS bytes) of the
+    library's m = 1 launch for one GEMV -- the launch-shape choice of the HIP library restated
+    for labelling profiles.  The configuration is the template-argument text that rocprofv3
+    prints in the kernel name (two launches can share grid and workgroup size)."""
+    mid = 8192 < in_f <= 24576
+    if arm == "q8_0":  # one wave per row; 4-wave workgroups up to 24576 columns
+        waves, split = (4 if in_f <= 24576 else 16), 1
+        cfg = ("QCfg<4, 1, 4, 1, 2, true, 8, 1, 1>" if in_f <= 8192 else
+               "QCfg<4, 1, 4, 3, 4, true, 8, 1, 1>" if mid else
+               "QCfg<16, 1, 4, 2, 3, true, 8, 1, 1>")
+    else:  # e4m3: 8-wave workgroups and two waves per row in the middle range
+        waves, split = (4 if in_f <= 8192 else (8 if mid else 16)), (2 if mid else 1)
+        cfg = ("Cfg<4, 1, 2, 2, 1, true, 8, 1, 1>" if in_f <= 8192 else
+               "Cfg<8, 1, 3, 3, 2, true, 8, 2, 1>" if mid else
+               "Cfg<16, 1, 4, 4, 4, true, 8, 1, 1>")
     wg = waves * 64
     grid = -(-out_f // (waves // split)) * wg
     if arm == "q8_0":
         nwin = -(-(in_f // 256) // 3)  # windows of 816 bytes (3 groups of 8 blocks)
         lds = nwin * 816 + (nwin * 24 + 8) * 4 + 48
-        return ("k_gemv_q8_0_fast", grid, wg, lds)
+        return ("k_gemv_q8_0_fast", cfg, grid, wg, lds)
     lds = -(-in_f // 1024) * 2176 + 32
-    return ("k_gemv_e4m3<true" if arm == "blk128" else "k_gemv_e4m3<false", grid, wg, lds)
+    return ("k_gemv_e4m3<true" if arm == "blk128" else "k_gemv_e4m3<false", cfg, grid, wg, lds)
 
 
 def _label_of(name: str, grid: int, wg: int, lds: int) -> str:
     for out_f, in_f in SHAPES:
         for arm in ARMS:
-            fam, g, w, _ = launch_signature(arm, out_f, in_f)
-            # rocprofv3 reports only static LDS, so (family, grid, workgroup) is the key; it is
-            # unique over the bench's nine launches.
-            if _short(name).startswith(fam) and (g, w) == (grid, wg):
+            fam, cfg, g, w, _ = launch_signature(arm, out_f, in_f)
+            # rocprofv3 reports only static LDS, so (family, configuration, grid, workgroup) is
+            # the key; it is unique over the bench's nine launches.
+            if _short(name).startswith(fam) and cfg in name and (g, w) == (grid, wg):
                 return f"{arm}@{out_f}x{in_f}"
     return "-"
 

@@ -423,11 +423,12 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
   return hipGetLastError();
 }
 
-// Shapes as for the e4m3 stream: 4 waves up to in_f = 8192, 8 up to 24576, 16 beyond, with
-// double-buffered batches of 4, 3 and 4 windows (a row of in_f = 5120 is 7 windows, the last one
-// two groups).  In the middle range two waves share each row (4 rows per workgroup): rows of
-// 17408 columns are 23 windows, and with one wave per row a 5120-row matrix would keep only
-// 20 long-lived waves per CU, unevenly spread.
+// Shapes measured on MI355X: one wave per row throughout, 4-wave workgroups up to in_f = 24576
+// and 16 beyond, with double-buffered batches of 4 windows (a row of in_f = 5120 is 7 windows,
+// the last one two groups; a row of 17408 is 23).  Unlike the e4m3 stream, the middle range
+// does not split rows between waves: with 816-byte windows, one wave per row in 4-wave
+// workgroups is 2-7% faster at 5120x17408, 2048x12288 and 5120x12288 than two waves per row
+// in 8-wave ones.
 // Several activation rows (m > 1) share each weight pass: up to 8 rows per workgroup for
 // in_f <= 8192, 2 beyond 8192 (LDS holds one staged row per activation row).  Every shape
 // used for one in_f range splits rows the same way (SPLIT), so each activation row is
@@ -436,8 +437,8 @@ using QSmall = QCfg<4, 1, 4, 1, 2, true>;                 // in_f <= 8192, m = 1
 using QSmallB2 = QCfg<4, 1, 3, 1, 2, true, 8, 1, 2>;      //               m = 2
 using QSmallB4 = QCfg<8, 1, 2, 1, 2, true, 6, 1, 4>;      //               m = 3..4
 using QSmallB8 = QCfg<8, 2, 1, 1, 3, true, 4, 1, 8>;      //               m >= 5
-using QMid = QCfg<8, 1, 3, 2, 3, true, 8, 2>;             // in_f <= 24576, m = 1
-using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 2, 2>;        //                m >= 2
+using QMid = QCfg<4, 1, 4, 3, 4, true>;                   // in_f <= 24576, m = 1
+using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 1, 2>;        //                m >= 2
 using QLarge = QCfg<16, 1, 4, 2, 3, true>;                // in_f <= 65536
 static_assert(QSmall::MAX_IN_F >= 8192 && QSmallB2::MAX_IN_F >= 8192 &&
                   QSmallB4::MAX_IN_F >= 8192 && QSmallB8::MAX_IN_F >= 8192 &&

@@ -30,11 +30,11 @@ def test_launch_labels_are_unique_over_the_step():
     sigs = {}
     for out_f, in_f in bench.SHAPES:
         for arm in bench.ARMS:
-            fam, grid, wg, _ = bench.launch_signature(arm, out_f, in_f)
-            key = (fam, grid, wg)
+            fam, cfg, grid, wg, _ = bench.launch_signature(arm, out_f, in_f)
+            key = (fam, cfg, grid, wg)
             assert key not in sigs, (key, sigs.get(key))
             sigs[key] = f"{arm}@{out_f}x{in_f}"
-            name = f"void fp8gemv::(anonymous namespace)::{fam}x, 1> >(int)"
+            name = f"void fp8gemv::(anonymous namespace)::{fam}, fp8gemv::{cfg} >(int)"
             assert bench._label_of(name, grid, wg, 0) == f"{arm}@{out_f}x{in_f}"
 
 
@@ -70,8 +70,8 @@ def test_summarize_pmc_scales_by_the_calibration_copy(tmp_path):
         fetch.append({**base, "Counter_Name": "FETCH_SIZE", "Counter_Value": str(f)})
         write.append({**base, "Counter_Name": "WRITE_SIZE", "Counter_Value": str(w)})
     add(1, "__amd_rocclr_copyBuffer", 131072, 512, known / 2, known)  # FETCH reads half
-    fam, grid, wg, _ = bench.launch_signature("q8_0", 5120, 17408)
-    add(2, f"void fp8gemv::(anonymous namespace)::{fam}x> >(int)", grid, wg, 46000.0, 40.0)
+    fam, cfg, grid, wg, _ = bench.launch_signature("q8_0", 5120, 17408)
+    add(2, f"void fp8gemv::(anonymous namespace)::{fam}<{cfg} >(int)", grid, wg, 46000.0, 40.0)
     fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
     _write_csv(fp, fetch)
     _write_csv(wp, write)
