@@ -193,3 +193,20 @@ def test_public_header_is_plain_c():
     r = subprocess.run(c_abi_build.compile_cmd("", syntax_only=True), capture_output=True,
                        text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_build_script_loads_without_the_package():
+    # build() must work on a fresh checkout, where the package (which refuses to import
+    # without its library) cannot be imported yet: its build script is loaded by path.
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import importlib.util, os, sys\n"
+            f"spec = importlib.util.spec_from_file_location('b', os.path.join({root!r}, "
+            "'fp8_gemv_amd', 'build.py'))\n"
+            "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+            "assert callable(m.build) and 'fp8_gemv_amd' not in sys.modules\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    src = open(os.path.join(root, "__graft_entry__.py")).read()
+    assert "from fp8_gemv_amd import build" not in src
