@@ -330,7 +330,7 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
 // used for one in_f range splits rows the same way (SPLIT), so each activation row is
 // computed in the same order whatever m is.
 using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;                // in_f <= 8192, m = 1
-using CfgSmallB2 = Cfg<4, 1, 2, 2, 1, true, 8, 1, 2>;     //               m = 2
+using CfgSmallB2 = Cfg<8, 1, 2, 1, 1, true, 8, 1, 2>;     //               m = 2
 using CfgSmallB4 = Cfg<8, 2, 1, 1, 1, true, 5, 1, 4>;     //               m = 3..4
 using CfgSmallB8 = Cfg<16, 2, 1, 1, 1, true, 4, 1, 8>;    //               m >= 5
 using CfgMid = Cfg<8, 1, 3, 3, 2, true, 8, 2>;            // in_f <= 24576, m = 1
