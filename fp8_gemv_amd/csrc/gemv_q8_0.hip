@@ -435,7 +435,7 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
 // computed in the same order whatever m is.
 using QSmall = QCfg<4, 1, 4, 1, 2, true>;                 // in_f <= 8192, m = 1
 using QSmallB2 = QCfg<4, 1, 3, 1, 2, true, 8, 1, 2>;      //               m = 2
-using QSmallB4 = QCfg<8, 1, 2, 1, 2, true, 6, 1, 4>;      //               m = 3..4
+using QSmallB4 = QCfg<4, 1, 2, 1, 2, true, 6, 1, 4>;      //               m = 3..4
 using QSmallB8 = QCfg<8, 2, 1, 1, 3, true, 4, 1, 8>;      //               m >= 5
 using QMid = QCfg<4, 1, 4, 3, 4, true>;                   // in_f <= 24576, m = 1
 using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 1, 2>;        //                m >= 2
