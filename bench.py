@@ -236,11 +236,17 @@ CALIB_MIB = 512
 
 
 def gemv_source_hash() -> str:
+    """Hash of the GEMV sources with comments and whitespace removed: any change to the code
+    changes it, an edit of a comment does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in GEMV_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -326,7 +326,7 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
 // flight; 6% faster at 5120 x 17408); 16 waves beyond.  All double-buffer their windows
 // (2 to 4 per batch) and fit 64 VGPRs.
 // Several activation rows (m > 1) share each weight pass: up to 8 rows per workgroup for
-// in_f <= 8192, 2 beyond 8192 (LDS holds one staged row per activation row).  Every shape
+// in_f <= 8192, 2 up to 24576 and 1 beyond (LDS holds one staged row per activation row).  Every shape
 // used for one in_f range splits rows the same way (SPLIT), so each activation row is
 // computed in the same order whatever m is.
 using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;                // in_f <= 8192, m = 1

@@ -430,7 +430,7 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
 // workgroups is 2-7% faster at 5120x17408, 2048x12288 and 5120x12288 than two waves per row
 // in 8-wave ones.
 // Several activation rows (m > 1) share each weight pass: up to 8 rows per workgroup for
-// in_f <= 8192, 2 beyond 8192 (LDS holds one staged row per activation row).  Every shape
+// in_f <= 8192, 2 up to 24576 and 1 beyond (LDS holds one staged row per activation row).  Every shape
 // used for one in_f range splits rows the same way (SPLIT), so each activation row is
 // computed in the same order whatever m is.
 using QSmall = QCfg<4, 1, 4, 1, 2, true>;                 // in_f <= 8192, m = 1
