@@ -67,13 +67,22 @@ __device__ __forceinline__ double lane_f64(double v, int lane) {
 __device__ double row_scale(const float *__restrict__ x, int ncols, float eps, double *red) {
   double hi = 0.0, lo = 0.0;
   constexpr int kBatch = 8;  // loads issued together before they are accumulated
-  for (int base = threadIdx.x * 4; base < ncols; base += kBatch * kColsPerPass) {
-    float4 v[kBatch];
+  // Batches of kBatch loads; the next batch is issued before the current one is accumulated,
+  // so a long row costs one load latency, not one per batch.  The elements are accumulated
+  // in the same order either way.
+  auto load_batch = [&](float4 (&v)[kBatch], int base) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int j = base + u * kColsPerPass;
       v[u] = j < ncols ? *reinterpret_cast<const float4 *>(x + j) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  };
+  float4 v[kBatch];
+  load_batch(v, threadIdx.x * 4);
+  for (int base = threadIdx.x * 4; base < ncols; base += kBatch * kColsPerPass) {
+    float4 nv[kBatch];
+    const int next = base + kBatch * kColsPerPass;
+    if (next < ncols) load_batch(nv, next);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -86,6 +95,8 @@ __device__ double row_scale(const float *__restrict__ x, int ncols, float eps, d
         lo += e;
       }
     }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = nv[u];
   }
   // Across the wave: DPP within each row of 16 lanes (quad swaps, then rotations by 4 and
   // 8), then the four row sums from lanes 0, 16, 32, 48 added in that fixed order.  Lanes of
