@@ -3,24 +3,20 @@
 // Source: docs.rs, memra-engine 0.125.0, src/bin/gemv_e4m3_bench.rs -- module doc QUESTION (the
 // ship path dequantises FP8 checkpoints to a Q8_0 slab at load: an fp16 scale then 32 int8 per
 // 32 weights, 34 bytes) and THE BLOCK-128 ARM (the per-tile f32 grid of block-scaled
-// checkpoints).  The page gives no formula; this takes the q8_1 block rule with the scale
-// stored as fp16.  Per 32-block of row r, all in f32:
+// checkpoints).  The page gives no formula; this takes the 32-value int8 block rule of the gate
+// page's q8_1 quantiser (q8_fuse_gate.rs, the `id = 1/d` branch) with the scale stored as fp16.
+// Per 32-block of row r, all in f32:
 //   v_i = e4m3(W[r, 32b + i]) * S      S = scale, or grid[r / 128, b / 4]
-//   d   = max_i |v_i| / 127
-//   q_i = round(v_i / d), halves away from zero (0 when d == 0)
+//   d   = max_i |v_i| / 127,  id = 1 / d (0 when d == 0)
+//   q_i = round(v_i * id), halves away from zero
 //   out = binary16(d) (round to nearest even, little-endian), then the 32 q_i as int8
+// d and id are IEEE f32 quotients (HIP's default division is correctly rounded) and the file is
+// compiled without contraction, so every step rounds exactly once, as written.
 //
-// gfx950 design: 1 byte read, 1.0625 bytes written per weight.  The 32 correctly rounded
-// quotients v_i / d of a block share d, so each is formed from one IEEE reciprocal per block
-// and one remainder correction (Markstein): q0 = v * (1/d), q = fma(fma(-q0, d, v), 1/d, q0).
-// With v and d first scaled by the same power of two (2^64 when d < 2^-60, 2^-64 when
-// d > 2^60), which changes neither the quotient nor anything else, the remainder never
-// reaches the subnormals, and q is the IEEE quotient for every e4m3 value and scale (checked
-// exhaustively per scale on the host; a -0 quotient may come back +0, which rounds to the
-// same integer).  One thread per block, 256 blocks per workgroup; a workgroup's 256 * 34 output bytes
-// are contiguous in the row, so they are assembled in LDS and written back with coalesced
-// 16-byte stores when the row layout allows it (in_f % 256 == 0, 16-byte aligned rows), 2-byte
-// stores otherwise.
+// gfx950 design: 1 byte read, 1.0625 bytes written per weight.  One thread per block, 256
+// blocks per workgroup; a workgroup's 256 * 34 output bytes are contiguous in the row, so they
+// are assembled in LDS and written back with coalesced 16-byte stores when the row layout
+// allows it (in_f % 256 == 0, 16-byte aligned rows), 2-byte stores otherwise.
 #include "common.hpp"
 
 namespace fp8gemv {
@@ -75,19 +71,11 @@ __global__ __launch_bounds__(kThreads) void k_requant_q8_0(
   uint16_t *dst = out16 + threadIdx.x * (kBlk / 2);
   if (b < nb) {
     dst[0] = __builtin_bit_cast(uint16_t, d16);
-    const float k = d < 0x1p-60f ? 0x1p64f : (d > 0x1p60f ? 0x1p-64f : 1.0f);
-    const float ds = d * k;
-    const float rcp = d != 0.0f ? 1.0f / ds : 0.0f;
-    auto quant = [&](float x) {
-      const float xs = x * k;
-      const float q0 = xs * rcp;
-      const float q = fmaf(fmaf(-q0, ds, xs), rcp, q0);  // the IEEE quotient x / d
-      return d != 0.0f ? (int)roundf(q) : 0;
-    };
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; i += 2) {
-      const int q0 = quant(v[i]);
-      const int q1 = quant(v[i + 1]);
+      const int q0 = (int)roundf(v[i] * id);
+      const int q1 = (int)roundf(v[i + 1] * id);
       dst[1 + i / 2] = (uint16_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8));
     }
   }

@@ -163,14 +163,17 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
  * requant_e4m3_q8_0 -- load-time requantisation of a raw e4m3 weight plane (per-tensor scale)
  * into ggml Q8_0 rows, the container gemv_q8_0_q81 reads.
  * Source: gemv_e4m3_bench.rs, module doc QUESTION (the ship path dequantises FP8 checkpoints
- * to a Q8_0 slab at load).  The page gives no formula; the rule is the q8_1 block rule with
- * the scale stored as fp16.  Per 32-block b of row r, in f32:
- *   v_i = e4m3(W[r, 32b + i]) * scale,  d = max|v_i| / 127,
- *   q_i = round(v_i / d) with halves away from zero (0 when d == 0),
+ * to a Q8_0 slab at load).  The page gives no formula; the rule is the 32-value block rule of
+ * quantize_q8_1 (q8_fuse_gate.rs, the `id = 1/d` branch) with the scale stored as fp16.  Per
+ * 32-block b of row r, every step in f32:
+ *   v_i = e4m3(W[r, 32b + i]) * scale,  d = max|v_i| / 127,  id = 1 / d (0 when d == 0),
+ *   q_i = round(v_i * id) with halves away from zero,
  *   Wq[r] bytes 34b .. 34b+33 = binary16(d) (round to nearest even, little-endian), q_0..q_31.
  *   W            u8 [out_f] rows of row_bytes bytes (first in_f used); 16-byte aligned,
  *                row_bytes >= in_f and a multiple of 16
- *   scale        finite (documented, not checked)
+ *   scale        finite, and 0 or of magnitude at least 2^-112 (documented, not checked: below
+ *                that a block's d can be so small that 1 / d overflows, and its bytes are then
+ *                unspecified)
  *   Wq           output rows of q_row_bytes bytes: only the first in_f / 32 * 34 bytes of each
  *                row are written; 2-byte aligned, q_row_bytes >= in_f / 32 * 34 and even; must
  *                not overlap W.  Wq 16-byte aligned with q_row_bytes % 16 == 0 and
@@ -184,7 +187,8 @@ int requant_e4m3_q8_0(const uint8_t *W, int64_t row_bytes, float scale, void *Wq
  * requant_e4m3_blk128_q8_0 -- the same for a block-128 scaled plane: the block's S is
  * grid[r / 128, b / 4] (each 32-block lies in one 128-column tile).
  * Source: as above, plus THE BLOCK-128 ARM (the f32 [ceil(out_f/128), ceil(in_f/128)] grid).
- *   grid       f32 [ceil(out_f/128), grid_cols], row-major, finite; 4-byte aligned
+ *   grid       f32 [ceil(out_f/128), grid_cols], row-major; every value obeys the rule for
+ *              scale above; 4-byte aligned
  *   grid_cols  must equal ceil(in_f / 128)
  *   other arguments as for requant_e4m3_q8_0
  */

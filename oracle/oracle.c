@@ -230,15 +230,18 @@ uint16_t oracle_f32_to_fp16(float f) {
 /*
  * Load-time requantisation of an e4m3 weight plane into ggml Q8_0 rows (the bench page's ship
  * path, QUESTION: FP8 checkpoints are dequantised to a Q8_0 slab at load, 34 bytes per 32
- * weights).  The page gives no formula; the plainest reading, taken here, is the same per-block
- * rule as the q8_1 quantiser with the scale stored as fp16:
+ * weights).  The page gives no formula.  The reading taken here is the one block rule the pages
+ * do show for 32-value int8 blocks, the q8_1 quantiser of the gate page with its `id = 1/d`
+ * branch, with the scale stored as fp16 (the Q8_0 container's scale type):
  *   v_i  = e4m3(W[r, 32b+i]) * S          f32 multiply; S = scale, or grid[r/128, b/4] when a
  *                                         block-128 grid is given (THE BLOCK-128 ARM)
  *   amax = max |v_i|,  d = amax / 127     f32
- *   q_i  = round(v_i / d), halves away from zero (0 when d == 0)
+ *   id   = 1 / d  (0 when d == 0)         f32
+ *   q_i  = round(v_i * id), halves away from zero
  *   block bytes: fp16(d) little-endian, then the 32 int8 q_i.
  * Rows r0 <= r < r1 are written at Wq + r * q_row_bytes.
- * Returns 0, -1 for an e4m3 NaN code or a non-finite scale (refused input), -2 on bad shapes.
+ * Returns 0, -1 for a refused input (an e4m3 NaN code, a non-finite scale, or a block whose
+ * d is so small that 1 / d overflows f32, which needs |S| below 2^-112), -2 on bad shapes.
  */
 int oracle_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                         int grid_cols, uint8_t *Wq, int64_t q_row_bytes, int in_f, int out_f,
@@ -262,11 +265,13 @@ int oracle_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const 
                 if (a > amax) amax = a;
             }
             float db = amax / 127.0f;
+            float id = (db != 0.0f) ? 1.0f / db : 0.0f;
+            if (!isfinite(id)) return -1;
             uint16_t h = oracle_f32_to_fp16(db);
             out[34 * b] = (uint8_t)(h & 0xFF);
             out[34 * b + 1] = (uint8_t)(h >> 8);
             for (int i = 0; i < 32; ++i) {
-                int8_t q = (db != 0.0f) ? (int8_t)roundf(v[i] / db) : 0;
+                int8_t q = (int8_t)roundf(v[i] * id);
                 out[34 * b + 2 + i] = (uint8_t)q;
             }
         }

@@ -326,8 +326,10 @@ def test_gemv_refuses_nan_codes():
 
 # --------------------------------------------------------------------- requantiser
 # e4m3 -> Q8_0 at load (gemv_e4m3_bench.rs, QUESTION: the ship path dequantises FP8 checkpoints
-# to a Q8_0 slab).  The page gives no formula; the oracle takes the q8_1 block rule with an fp16
-# scale.  Pinned by hand-worked blocks, numpy's binary16 rounding, exact rationals and bounds.
+# to a Q8_0 slab).  The page gives no formula; the oracle takes the q8_1 block rule (id = 1/d,
+# q = round(v * id)) with an fp16 scale.  Pinned by hand-worked blocks (three of them hold an
+# element at half the block maximum, where the reciprocal and a plain division round apart),
+# numpy's binary16 rounding, exact rationals and bounds.
 
 def _read_requant_blocks():
     import os
@@ -352,7 +354,7 @@ def _read_requant_blocks():
 
 def test_requant_golden_blocks():
     blocks = _read_requant_blocks()
-    assert len(blocks) >= 5
+    assert len(blocks) >= 8
     for blk in blocks:
         W = np.array([blk["codes"]], dtype=np.uint8)
         out = oracle.requant_q8_0(W, 32, 32, 1, scale=blk["S"])[0]
