@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import case, dev, host, to_dev
+from gpu_util import case, dev, host, oracle_all_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,10 @@ class Case:
                                     self.in_f, self.out_f)
         return host(y)
 
+    def oracle_all(self):
+        """The oracle over every output row, rows split across host threads."""
+        return oracle_all_rows(lambda rows: self.oracle(rows), self.out_f)
+
     def oracle(self, rows=None):
         if self.kind == "q8_0":
             return oracle.gemv_q8_0(self.W, self.row_bytes, self.qs, self.d, self.in_f,
@@ -100,40 +104,37 @@ def test_gemv_small_shapes_match_oracle(fg, kind, out_f, in_f, m):
     _assert_close(y, yo, A)
 
 
-# The 27B-class projection shapes of the bench, m = 1, the same launch as bench.py; outputs
-# sampled in three row ranges (start, middle, end) that the oracle computes exactly.
+# The 27B-class projection shapes of the bench, m = 1, the same launch as bench.py; every
+# output against the oracle (run over all rows, split across host threads).
 FULL = [(5120, 5120), (17408, 5120), (5120, 17408)]
 
 
 @pytest.mark.parametrize("out_f,in_f", FULL)
 @pytest.mark.parametrize("kind", KINDS)
-def test_gemv_full_shapes_sampled_rows(fg, kind, out_f, in_f):
+def test_gemv_full_shapes_every_row(fg, kind, out_f, in_f):
     case(f"{kind} full out_f={out_f} in_f={in_f}")
     c = Case(kind, out_f, in_f, 1)
     y = c.gpu(fg)
     assert np.all(np.isfinite(y))
-    for r0 in (0, out_f // 2 - 37, out_f - 96):
-        rows = (r0, r0 + 96)
-        yo, A = c.oracle(rows)
-        _assert_close(y, yo, A, rows)
+    yo, A = c.oracle_all()
+    _assert_close(y, yo, A)
 
 
-# The projection shapes of the 27B and 1.7B sheets not covered above ([out_f, in_f]).
+# The projection shapes of the 27B and 1.7B sheets not covered above ([out_f, in_f]), every
+# output.
 SHEET = [(12288, 5120), (1024, 5120), (5120, 6144), (2048, 2048), (1024, 2048), (6144, 2048),
          (2048, 6144)]
 
 
 @pytest.mark.parametrize("out_f,in_f", SHEET)
 @pytest.mark.parametrize("kind", KINDS)
-def test_gemv_sheet_shapes_sampled_rows(fg, kind, out_f, in_f):
+def test_gemv_sheet_shapes_every_row(fg, kind, out_f, in_f):
     case(f"{kind} sheet out_f={out_f} in_f={in_f}")
     c = Case(kind, out_f, in_f, 1)
     y = c.gpu(fg)
     assert np.all(np.isfinite(y))
-    for r0 in (0, out_f // 2 - 37, out_f - 64):
-        rows = (r0, r0 + 64)
-        yo, A = c.oracle(rows)
-        _assert_close(y, yo, A, rows)
+    yo, A = c.oracle_all()
+    _assert_close(y, yo, A)
 
 
 # m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
@@ -148,8 +149,9 @@ def test_gemv_m_rows_bit_identical_to_m1(fg, kind, out_f, in_f):
         for t in range(m):
             y1 = c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)
             assert y[t].tobytes() == y1[0].tobytes(), (m, t)
-    yo, A = c.oracle((1000, 1100))
-    _assert_close(y, yo, A, (1000, 1100))
+    # the last call (m = 11, two weight passes) against the oracle at every output
+    yo, A = c.oracle_all()
+    _assert_close(y, yo, A)
 
 
 @pytest.mark.parametrize("kind", KINDS)

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import case, dev, host, to_dev
+from gpu_util import case, dev, host, oracle_threads, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -55,21 +55,29 @@ def test_requant_matches_oracle_bytes(fg, arm, out_f, in_f):
     assert np.array_equal(got, want)
 
 
-# The 27B-class projection shapes, sampled rows (start, middle, end) against the oracle.
+# The 27B-class projection shapes, every row against the oracle (rows split across host
+# threads; each oracle call writes only its own rows).
 @pytest.mark.parametrize("out_f,in_f", [(5120, 5120), (17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("arm", ["scale_pow2", "blk128"])
-def test_requant_full_shapes_sampled_rows(fg, arm, out_f, in_f):
+def test_requant_full_shapes_every_row(fg, arm, out_f, in_f):
+    import concurrent.futures as cf
     case(f"requant full {arm} out_f={out_f} in_f={in_f}")
     W = synth.e4m3_weights(out_f, in_f)
     grid = synth.blk128_grid(out_f, in_f) if arm == "blk128" else None
     got = _run(fg, W, in_f, out_f, scale=None if grid is not None else 2.0 ** -4, grid=grid)
-    for r0 in (0, out_f // 2 - 37, out_f - 64):
-        rows = (r0, r0 + 64)
+
+    def part(rows):
         if grid is not None:
-            want = oracle.requant_q8_0(W, in_f, in_f, out_f, grid=grid, rows=rows)
-        else:
-            want = oracle.requant_q8_0(W, in_f, in_f, out_f, scale=2.0 ** -4, rows=rows)
-        assert np.array_equal(got[r0:r0 + 64], want[r0:r0 + 64])
+            return oracle.requant_q8_0(W, in_f, in_f, out_f, grid=grid, rows=rows)
+        return oracle.requant_q8_0(W, in_f, in_f, out_f, scale=2.0 ** -4, rows=rows)
+
+    nth = oracle_threads()
+    step = (out_f + nth - 1) // nth
+    ranges = [(r, min(out_f, r + step)) for r in range(0, out_f, step)]
+    with cf.ThreadPoolExecutor(max_workers=nth) as ex:
+        parts = list(ex.map(part, ranges))
+    for (r0, r1), want in zip(ranges, parts):
+        assert np.array_equal(got[r0:r1], want[r0:r1]), (r0, r1)
 
 
 def test_requant_padded_and_unaligned_rows_leave_padding_alone(fg):
