@@ -51,6 +51,19 @@ MAX_M = max(M_ROWS)
 SHAPE_M = (17408, 5120)
 
 
+# Spin before a queue of individually timed launches: ~10 ms at the shader clock, longer than
+# the host needs to queue 200 launches with their events.
+SPIN_CYCLES = 20_000_000
+
+
+def percentile(sorted_vals, q: float) -> float:
+    """Nearest-rank percentile of an ascending list (q in 0..100)."""
+    if not sorted_vals:
+        raise ValueError("no values")
+    k = max(0, min(len(sorted_vals) - 1, math.ceil(q / 100 * len(sorted_vals)) - 1))
+    return sorted_vals[k]
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -260,28 +273,15 @@ def _kernel_key(name: str, grid: str, wg: str) -> str:
 
 def launch_signature(arm: str, out_f: int, in_f: int):
     """(kernel family, launch configuration, grid threads, workgroup size, LDS bytes) of the
-    library's m = 1 launch for one GEMV -- the launch-shape choice of the HIP library restated
-    for labelling profiles.  The configuration is the template-argument text that rocprofv3
-    prints in the kernel name (two launches can share grid and workgroup size)."""
-    mid = 8192 < in_f <= 24576
-    if arm == "q8_0":  # one wave per row; 4-wave workgroups up to 24576 columns
-        waves, split = (4 if in_f <= 24576 else 16), 1
-        cfg = ("QCfg<4, 1, 4, 1, 2, true, 8, 1, 1>" if in_f <= 8192 else
-               "QCfg<4, 1, 4, 3, 4, true, 8, 1, 1>" if mid else
-               "QCfg<16, 1, 4, 2, 3, true, 8, 1, 1>")
-    else:  # e4m3: 8-wave workgroups and two waves per row in the middle range
-        waves, split = (4 if in_f <= 8192 else (8 if mid else 16)), (2 if mid else 1)
-        cfg = ("Cfg<4, 1, 2, 2, 1, true, 8, 1, 1>" if in_f <= 8192 else
-               "Cfg<8, 1, 3, 3, 2, true, 8, 2, 1>" if mid else
-               "Cfg<16, 1, 4, 4, 4, true, 8, 1, 1>")
-    wg = waves * 64
-    grid = -(-out_f // (waves // split)) * wg
-    if arm == "q8_0":
-        nwin = -(-(in_f // 256) // 3)  # windows of 816 bytes (3 groups of 8 blocks)
-        lds = nwin * 816 + (nwin * 24 + 8) * 4 + 48
-        return ("k_gemv_q8_0_fast", cfg, grid, wg, lds)
-    lds = -(-in_f // 1024) * 2176 + 32
-    return ("k_gemv_e4m3<true" if arm == "blk128" else "k_gemv_e4m3<false", cfg, grid, wg, lds)
+    library's m = 1 launch for one GEMV, as the library reports it (fp8gemv_gemv_launch_info:
+    the same selection code that launches fills it in), for labelling profiles.  The
+    configuration is the template-argument text that rocprofv3 prints in the kernel name (two
+    launches can share grid and workgroup size)."""
+    import fp8_gemv_amd as fg
+    row_bytes = (in_f // 32) * 34 if arm == "q8_0" else in_f
+    info = fg.gemv_launch_info(arm, row_bytes, 1, in_f, out_f)
+    grid = info["grid_x"] * info["workgroup_size"]
+    return (info["kernel"], info["config"], grid, info["workgroup_size"], info["lds_bytes"])
 
 
 def _label_of(name: str, grid: int, wg: int, lds: int) -> str:
@@ -437,6 +437,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--kernel-iters", type=int, default=60,
                     help="back-to-back launches per (shape, container) for per-kernel timing")
+    ap.add_argument("--launches", type=int, default=200,
+                    help="rotated launches per GEMV timed one by one (median, p10, p90)")
+    ap.add_argument("--no-read-patterns", action="store_true",
+                    help="skip the read-pattern ceiling study")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--shapes", default="all", help="comma list like 17408x5120 (out x in)")
@@ -533,6 +537,34 @@ def main() -> int:
         torch.cuda.synchronize()
         return g
 
+    def graph_us(launch, n, reps=5):
+        """n back-to-back launches launch(0..n-1) captured in one graph, replayed once untimed
+        and then `reps` times, each replay between HIP events on the launch stream; returns the
+        median over replays of the mean us per launch, and all replay means."""
+        g = capture(lambda: [launch(i) for i in range(n)])
+        g.replay()
+        ts = sorted(timed(g.replay, n) * 1e3 for _ in range(reps))
+        del g
+        return ts[len(ts) // 2], ts
+
+    def per_launch_us(launch, n=200):
+        """n launches, each between its own pair of HIP events on the launch stream.  A spin
+        kernel goes first so that the host queues all of them before the device reaches them
+        (the gap between one launch's end event and the next one's start event shows whether
+        it did).  Returns the sorted per-launch us and the median gap in us."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        for i in range(n):
+            evs[i][0].record(stream)
+            launch(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        gaps = sorted(evs[i][1].elapsed_time(evs[i + 1][0]) * 1e3 for i in range(n - 1))
+        return t, gaps[len(gaps) // 2]
+
     def run_m_rows():
         """Small-batch rows (gemv_e4m3_bench.rs: m in {1, 2, 4, 8} through grid.y at
         17408x5120): m activation rows from the producer with nrows = m, one GEMV call per
@@ -608,9 +640,10 @@ def main() -> int:
     for (out_f, in_f, a), obj in arm_objs.items():
         qs, d = producer((out_f, in_f))
         n = max(args.kernel_iters, obj.copies)
-        g = capture(lambda: [obj.launch(qs, d) for _ in range(n)])
-        g.replay()
-        us = timed(g.replay, n) * 1e3
+        us, reps = graph_us(lambda i: obj.launch(qs, d), n)
+        # The page's statistic: the median (and p10 / p90) of per-launch times over
+        # args.launches rotated launches, each timed on its own.
+        per, gap = per_launch_us(lambda i: obj.launch(qs, d), args.launches)
         # The pages' own protocol for comparison: host clock around launch + synchronize,
         # median over iterations (includes launch and synchronisation latency).
         walls = []
@@ -624,8 +657,14 @@ def main() -> int:
             "us": round(us, 3), "weight_GBs": round(wb / us / 1e3, 1),
             "pct_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1),
             "alg_bytes": algorithmic_bytes(a, out_f, in_f), "copies": obj.copies, "launches": n,
+            "graph_replay_us": [round(t, 3) for t in reps],
+            "median_us": round(percentile(per, 50), 3), "p10_us": round(percentile(per, 10), 3),
+            "p90_us": round(percentile(per, 90), 3), "per_launch_mean_us": round(sum(per) / len(per), 3),
+            "per_launch_n": len(per), "per_launch_gap_us_median": round(gap, 3),
             "host_wall_us_median": round(sorted(walls)[len(walls) // 2], 1)}
-        log(f"{a:7s} {out_f}x{in_f}: {us:8.2f} us  {wb / us / 1e3:7.1f} GB/s")
+        log(f"{a:7s} {out_f}x{in_f}: {us:8.2f} us  {wb / us / 1e3:7.1f} GB/s  "
+            f"per-launch median {percentile(per, 50):.2f} (p10 {percentile(per, 10):.2f}, "
+            f"p90 {percentile(per, 90):.2f}) us")
         if args.jsonl:
             with open(args.jsonl, "a") as f:
                 f.write(json.dumps({"arm": a, "out_f": out_f, "in_f": in_f,
@@ -707,51 +746,56 @@ def main() -> int:
             log(f"requant {a:6s} {out_f}x{in_f}: {us:8.2f} us  {moved / us / 1e3:7.1f} GB/s")
             del g, Wq
 
-    # Achievable read ceiling: the library's streaming-read measurement kernel over the same
-    # rotated e4m3 copies (same bytes, same load pattern, no arithmetic).
-    ceiling = {}
+    # Achievable read ceiling: the library's streaming-read measurement kernels in every load
+    # pattern, each over four sizes (26, 89, 178 and 356 MB; the Q8_0 rows pattern over the
+    # Q8_0 planes of the same shapes and their multiples), cold by rotation, each fitted as
+    # t = fixed + bytes / steady.  The best pattern at each size is the ceiling the GEMVs are
+    # compared with.
+    ceiling, read_patterns, read_fit = {}, {}, None
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    for (out_f, in_f, a), obj in arm_objs.items():
-        if a != "e4m3":
-            continue
-        nbytes = weight_bytes(a, out_f, in_f)
-        n = max(args.kernel_iters, obj.copies)
-        g = capture(lambda: [fg.fp8gemv_read_bytes(obj.W[i % obj.copies], nbytes, sink)
-                             for i in range(n)])
-        g.replay()
-        us = timed(g.replay, n) * 1e3
-        ceiling[f"{out_f}x{in_f}"] = {"bytes": nbytes, "us": round(us, 3),
-                                      "GBs": round(nbytes / us / 1e3, 1),
-                                      "pct_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1)}
-        log(f"read    {out_f}x{in_f}: {us:8.2f} us  {nbytes / us / 1e3:7.1f} GB/s (ceiling)")
+    if not (args.kernels_only or args.no_read_patterns):
+        e4_small, e4 = weight_bytes("e4m3", 5120, 5120), weight_bytes("e4m3", 17408, 5120)
+        q8_small, q8 = weight_bytes("q8_0", 5120, 5120), weight_bytes("q8_0", 17408, 5120)
+        pools = {}
+
+        def pool(nbytes):
+            if nbytes not in pools:
+                pools[nbytes] = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev)
+                                 for _ in range(n_copies(nbytes))]
+            return pools[nbytes]
+        for pat, rb, sizes in (("chunk8k", 0, None), ("chunk16k", 0, None), ("wg8", 0, None),
+                               ("wg16", 0, None), ("persistent", 0, None), ("cached", 0, None),
+                               ("rows_1k", 5120, None),
+                               ("rows_816", 5440, (q8_small, q8, 2 * q8, 4 * q8))):
+            pts = []
+            for nbytes in sizes or (e4_small, e4, 2 * e4, 4 * e4):
+                bufs = pool(nbytes)
+                us, _ = graph_us(lambda i: fg.fp8gemv_read_pattern(
+                    bufs[i % len(bufs)], nbytes, pat, sink, row_bytes=rb),
+                    max(args.kernel_iters // 2, len(bufs)), reps=3)
+                pts.append((nbytes, round(us, 3)))
+            read_patterns[pat] = fit_read_ceiling(pts)
+            log(f"read {pat:10s}: " + ", ".join(f"{b / 1e6:.1f} MB {t:.2f} us" for b, t in pts)
+                + f"; steady {read_patterns[pat]['steady_GBs']} GB/s, fixed "
+                  f"{read_patterns[pat]['fixed_us']} us")
+        del pools
+        torch.cuda.empty_cache()
+        for shape, nbytes in (("5120x5120", e4_small), ("17408x5120", e4), ("5120x17408", e4)):
+            best = min(((p, pt["us"]) for p, f in read_patterns.items() if p != "rows_816"
+                        for pt in f["points"] if pt["bytes"] == nbytes), key=lambda x: x[1])
+            ceiling[shape] = {"bytes": nbytes, "us": best[1], "pattern": best[0],
+                              "GBs": round(nbytes / best[1] / 1e3, 1),
+                              "pct_peak": round(100 * nbytes / best[1] / 1e3 / HBM_PEAK_GBS, 1)}
+        best_pat = min((p for p in read_patterns if p != "rows_816"),
+                       key=lambda p: next(pt["us"] for pt in read_patterns[p]["points"]
+                                          if pt["bytes"] == e4))
+        read_fit = dict(read_patterns[best_pat], pattern=best_pat)
+        log(f"read ceiling: best pattern at 89 MB {best_pat}: steady {read_fit['steady_GBs']} "
+            f"GB/s ({read_fit['steady_pct_peak']}%), fixed {read_fit['fixed_us']} us per launch")
     for k, v in detail.items():
         shape = k.split("@")[1]
         if shape in ceiling:
             v["pct_of_read_ceiling"] = round(100 * (v["weight_GBs"] / ceiling[shape]["GBs"]), 1)
-
-    # The read ceiling as a function of size: the same kernel over 2x and 4x the 89 MB plane,
-    # cold by rotation, fitted as t = fixed + bytes / steady.  The fit says how much of the gap
-    # to peak is a per-launch cost and how much is the stream rate itself.
-    read_fit = None
-    if not args.kernels_only and ceiling:
-        pts = [(v["bytes"], v["us"]) for v in ceiling.values()]
-        for mult in (2, 4):
-            nbytes = mult * weight_bytes("e4m3", 17408, 5120)
-            copies = n_copies(nbytes)
-            bufs = [torch.full((nbytes,), 0x11, dtype=torch.uint8, device=dev)
-                    for _ in range(copies)]
-            n = max(args.kernel_iters // 2, copies)
-            g = capture(lambda: [fg.fp8gemv_read_bytes(bufs[i % copies], nbytes, sink)
-                                 for i in range(n)])
-            g.replay()
-            us = timed(g.replay, n) * 1e3
-            pts.append((nbytes, round(us, 3)))
-            log(f"read    {nbytes / 1e6:7.1f} MB: {us:8.2f} us  {nbytes / us / 1e3:7.1f} GB/s")
-            del g, bufs
-            torch.cuda.empty_cache()
-        read_fit = fit_read_ceiling(pts)
-        log(f"read fit: steady {read_fit['steady_GBs']} GB/s ({read_fit['steady_pct_peak']}%), "
-            f"fixed {read_fit['fixed_us']} us per launch")
 
     # Producer alone (latency-bound; the gate page's site widths), fused vs two-launch chain.
     prod_us = {}
@@ -805,7 +849,7 @@ def main() -> int:
     # DISCIPLINE): (a) per-launch time with 512 MB pushed through the device right before each
     # launch must match the rotation's; (b) the time over a growing number of rotated copies
     # must plateau once the rotation set exceeds the last-level cache.
-    cold = {}
+    cold, fixed = {}, {}
     key = (17408, 5120, "e4m3")
     if key in arm_objs and not args.kernels_only:
         obj = arm_objs[key]
@@ -830,7 +874,42 @@ def main() -> int:
                 torch.cuda.synchronize()
                 per.append(e0.elapsed_time(e1) * 1e3)
             cold[label] = round(sorted(per)[len(per) // 2], 3)
-        del src, dst
+
+        # The fixed cost of a launch taken apart: the 89 MB pattern's grid with no loads
+        # (dispatch and drain), and one wave reading 1 KiB (a launch plus one round trip to
+        # memory), each alone between its own events after the spin (warm) or after the scrub
+        # (cold), and back to back in a graph.
+        e4 = weight_bytes("e4m3", 17408, 5120)
+        probe = torch.randint(0, 256, (e4,), dtype=torch.uint8, device=dev)
+        for name, pat in (("empty_grid", "empty"), ("one_wave_1KiB", "one_wave")):
+            for label, scrub in (("after_spin", False), ("after_scrub", True)):
+                per = []
+                for i in range(24):
+                    if scrub:
+                        dst.copy_(src)
+                    else:
+                        torch.cuda._sleep(200_000)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    if pat == "one_wave":  # 1 KiB at a new 4 KiB-aligned spot each time
+                        off = (i * 4096 * 97) % (e4 - 4096)
+                        fg.fp8gemv_read_pattern(probe[off:], 1024, pat, sink)
+                    else:
+                        fg.fp8gemv_read_pattern(probe, e4, pat, sink)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    per.append(e0.elapsed_time(e1) * 1e3)
+                fixed[f"{name}_{label}_us_median"] = round(sorted(per)[len(per) // 2], 3)
+            nb = e4 if pat == "empty" else 1024
+            us, _ = graph_us(lambda i: fg.fp8gemv_read_pattern(probe, nb, pat, sink),
+                             args.kernel_iters)
+            fixed[f"{name}_graph_us"] = round(us, 3)
+        fixed["note"] = ("empty_grid: the 2720-workgroup grid of the 89 MB read with no loads; "
+                         "one_wave_1KiB: one 64-lane wave loading 1 KiB; *_after_*: one launch "
+                         "between its own events; *_graph_us: mean of back-to-back launches")
+        log(f"fixed cost: {fixed}")
+        del src, dst, probe
         sweep = {}
         for c in sorted({1, 2, 4, obj.copies}):
             if c > obj.copies:
@@ -874,7 +953,8 @@ def main() -> int:
                    "eps": EPS, "e4m3_scale": SCALE},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
-        "gemv": detail, "read_ceiling": ceiling, "read_fit": read_fit, "m_rows": m_rows, "sheets": sheets,
+        "gemv": detail, "read_ceiling": ceiling, "read_fit": read_fit,
+        "read_patterns": read_patterns, "fixed_cost": fixed, "m_rows": m_rows, "sheets": sheets,
         "requant": requant,
         "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu, "cold_check": cold,

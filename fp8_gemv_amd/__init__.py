@@ -33,7 +33,21 @@ FP8GEMV_MAX_M = 65535
 EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "silu_mul_f32", "silu_mul_q8_1",
            "gemv_q8_0_q81", "gemv_e4m3_q81",
            "gemv_e4m3_blk128_q81", "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
-           "fp8gemv_read_bytes", "fp8gemv_strerror")
+           "fp8gemv_read_bytes", "fp8gemv_read_pattern", "fp8gemv_gemv_launch_info",
+           "fp8gemv_strerror")
+
+
+FP8GEMV_Q8_0 = 0
+FP8GEMV_E4M3 = 1
+FP8GEMV_E4M3_BLK128 = 2
+CONTAINERS = {"q8_0": FP8GEMV_Q8_0, "e4m3": FP8GEMV_E4M3, "blk128": FP8GEMV_E4M3_BLK128}
+
+
+class LaunchInfo(ctypes.Structure):
+    """fp8gemv_launch_info of the header."""
+    _fields_ = [("grid_x", ctypes.c_uint32), ("grid_y", ctypes.c_uint32),
+                ("workgroup_size", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32),
+                ("kernel", ctypes.c_char_p), ("config", ctypes.c_char_p)]
 
 
 class Fp8GemvError(RuntimeError):
@@ -69,6 +83,11 @@ def _load() -> ctypes.CDLL:
         fn.restype = i32
     lib.fp8gemv_read_bytes.argtypes = [vp, i64, vp, vp]
     lib.fp8gemv_read_bytes.restype = i32
+    lib.fp8gemv_read_pattern.argtypes = [vp, i64, i32, i64, vp, vp]
+    lib.fp8gemv_read_pattern.restype = i32
+    lib.fp8gemv_gemv_launch_info.argtypes = [i32, vp, i64, i32, i32, i32,
+                                             ctypes.POINTER(LaunchInfo)]
+    lib.fp8gemv_gemv_launch_info.restype = i32
     lib.fp8gemv_strerror.argtypes = [i32]
     lib.fp8gemv_strerror.restype = ctypes.c_char_p
     return lib
@@ -270,6 +289,49 @@ def fp8gemv_read_bytes(buf, nbytes: int, sink, stream=None) -> None:
     _run("fp8gemv_read_bytes", dev,
          _ptr(buf, "buf", torch.uint8, nbytes, dev), nbytes,
          _ptr(sink, "sink", torch.int32, 1, dev), _stream(stream, dev))
+
+
+# Load patterns of fp8gemv_read_pattern (the FP8GEMV_READ_* constants of the header).
+FP8GEMV_READ_CHUNK8K = 0
+FP8GEMV_READ_CHUNK16K = 1
+FP8GEMV_READ_WG8 = 2
+FP8GEMV_READ_WG16 = 3
+FP8GEMV_READ_PERSISTENT = 4
+FP8GEMV_READ_CACHED = 5
+FP8GEMV_READ_ROWS_1K = 6
+FP8GEMV_READ_ROWS_816 = 7
+FP8GEMV_READ_EMPTY = 8
+FP8GEMV_READ_ONE_WAVE = 9
+FP8GEMV_READ_NUM_PATTERNS = 10
+READ_PATTERNS = {"chunk8k": FP8GEMV_READ_CHUNK8K, "chunk16k": FP8GEMV_READ_CHUNK16K,
+                 "wg8": FP8GEMV_READ_WG8, "wg16": FP8GEMV_READ_WG16,
+                 "persistent": FP8GEMV_READ_PERSISTENT, "cached": FP8GEMV_READ_CACHED,
+                 "rows_1k": FP8GEMV_READ_ROWS_1K, "rows_816": FP8GEMV_READ_ROWS_816,
+                 "empty": FP8GEMV_READ_EMPTY, "one_wave": FP8GEMV_READ_ONE_WAVE}
+
+
+def fp8gemv_read_pattern(buf, nbytes: int, pattern: str, sink, row_bytes: int = 0,
+                         stream=None) -> None:
+    """Measurement aid: stream nbytes of buf in one of READ_PATTERNS (no result)."""
+    dev = _dev(buf)
+    _run("fp8gemv_read_pattern", dev,
+         _ptr(buf, "buf", torch.uint8, nbytes, dev), nbytes, READ_PATTERNS[pattern], row_bytes,
+         _ptr(sink, "sink", torch.int32, 1, dev), _stream(stream, dev))
+
+
+def gemv_launch_info(container: str, row_bytes: int, m: int, in_f: int, out_f: int,
+                     w_align: int = 256) -> dict:
+    """What the GEMV of `container` launches for these arguments (no device work): grid in
+    workgroups, threads per workgroup, dynamic LDS bytes, kernel family and configuration.
+    `w_align` is the weight pointer's alignment (it decides the Q8_0 fast path)."""
+    info = LaunchInfo()
+    rc = _lib.fp8gemv_gemv_launch_info(CONTAINERS[container], w_align, row_bytes, m, in_f, out_f,
+                                       ctypes.byref(info))
+    if rc != 0:
+        raise Fp8GemvError("fp8gemv_gemv_launch_info", rc, strerror(rc))
+    return {"grid_x": info.grid_x, "grid_y": info.grid_y, "workgroup_size": info.workgroup_size,
+            "lds_bytes": info.lds_bytes, "kernel": info.kernel.decode(),
+            "config": info.config.decode()}
 
 
 # ------------------------------------------------------------------------- byte counts

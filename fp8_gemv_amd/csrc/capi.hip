@@ -148,6 +148,46 @@ int fp8gemv_read_bytes(const void *p, int64_t bytes, uint32_t *sink, void *strea
   return launch_rc(fp8gemv::launch_read_bytes(p, bytes, sink, (hipStream_t)stream));
 }
 
+int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_bytes,
+                         uint32_t *sink, void *stream) {
+  if (!p || !sink) return FP8GEMV_ERR_NULL;
+  if (bytes < 1 || pattern < 0 || pattern >= FP8GEMV_READ_NUM_PATTERNS) return FP8GEMV_ERR_SHAPE;
+  if (pattern == FP8GEMV_READ_ROWS_1K || pattern == FP8GEMV_READ_ROWS_816) {
+    if (row_bytes < 1024 || row_bytes > (1 << 20) || row_bytes % 16 != 0 || bytes % row_bytes != 0)
+      return FP8GEMV_ERR_SHAPE;
+  }
+  if (bytes > FP8GEMV_MAX_READ_BYTES) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(p, 16) || !aligned(sink, 4)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(
+      fp8gemv::launch_read_pattern(p, bytes, pattern, row_bytes, sink, (hipStream_t)stream));
+}
+
+int fp8gemv_gemv_launch_info(int container, const void *W, int64_t row_bytes, int m, int in_f,
+                             int out_f, fp8gemv_launch_info *info) {
+  if (!W || !info) return FP8GEMV_ERR_NULL;
+  if (m < 1 || out_f < 1 || bad_cols(in_f)) return FP8GEMV_ERR_SHAPE;
+  if (in_f > FP8GEMV_MAX_IN_F || m > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
+  fp8gemv::LaunchDesc r;
+  if (container == FP8GEMV_Q8_0) {
+    if (row_bytes < (int64_t)(in_f / 32) * 34) return FP8GEMV_ERR_ROW_BYTES;
+    if (!aligned(W, 2) || row_bytes % 2 != 0) return FP8GEMV_ERR_ALIGN;
+    r = fp8gemv::describe_gemv_q8_0(static_cast<const uint8_t *>(W), row_bytes, m, in_f, out_f);
+  } else if (container == FP8GEMV_E4M3 || container == FP8GEMV_E4M3_BLK128) {
+    if (row_bytes < in_f) return FP8GEMV_ERR_ROW_BYTES;
+    if (!aligned(W, 16) || row_bytes % 16 != 0) return FP8GEMV_ERR_ALIGN;
+    r = fp8gemv::describe_gemv_e4m3(container == FP8GEMV_E4M3_BLK128, m, in_f, out_f);
+  } else {
+    return FP8GEMV_ERR_SHAPE;
+  }
+  info->grid_x = r.grid_x;
+  info->grid_y = r.grid_y;
+  info->workgroup_size = r.threads;
+  info->lds_bytes = r.lds;
+  info->kernel = r.kernel;
+  info->config = r.config;
+  return FP8GEMV_OK;
+}
+
 const char *fp8gemv_strerror(int rc) {
   switch (rc) {
     case FP8GEMV_OK: return "ok";

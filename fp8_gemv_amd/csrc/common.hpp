@@ -98,6 +98,32 @@ inline hipError_t set_lds_limit_once(const void *kernel, size_t bytes,
 }
 }  // namespace fp8gemv
 
+// -------------------------------------------------------------- launch descriptions ----
+// What a GEMV call launches, for profilers and benches: the same selection code that launches
+// fills it in, so it can never disagree with the launch.
+#include <cstdio>
+#include <string>
+namespace fp8gemv {
+struct LaunchDesc {
+  unsigned grid_x = 0, grid_y = 0, threads = 0, lds = 0;
+  const char *kernel = "";
+  const char *config = "";
+};
+template <class C> struct Tag { using type = C; };
+// The launch configuration type's text as it appears in the demangled kernel symbol, every
+// template argument written out, e.g. "Cfg<4, 1, 2, 2, 1, true, 8, 1, 1>" (static storage).
+// C provides NAME and the nine parameters P0..P8 in template-argument order (P5 a bool).
+template <class C> const char *config_text() {
+  static const std::string text = [] {
+    char b[128];
+    snprintf(b, sizeof b, "%s<%d, %d, %d, %d, %d, %s, %d, %d, %d>", C::NAME, C::P0, C::P1, C::P2,
+             C::P3, C::P4, C::P5 ? "true" : "false", C::P6, C::P7, C::P8);
+    return std::string(b);
+  }();
+  return text.c_str();
+}
+}  // namespace fp8gemv
+
 // --------------------------------------------------------------- internal launchers ----
 // Host-side launchers, one per kernel family; arguments are validated by the C ABI layer
 // before these run.  Each returns the hipError_t of the launch.
@@ -118,9 +144,13 @@ hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, co
                             float *y, int m, int in_f, int out_f, hipStream_t s);
 hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
                             const float *d, float *y, int m, int in_f, int out_f, hipStream_t s);
+LaunchDesc describe_gemv_e4m3(bool blk128, int m, int in_f, int out_f);
+LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f);
 hipError_t launch_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                                int grid_cols, bool blk128, void *Wq, int64_t q_row_bytes,
                                int in_f, int out_f, hipStream_t s);
 hipError_t launch_read_bytes(const void *p, int64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_bytes,
+                               uint32_t *sink, hipStream_t s);
 
 }  // namespace fp8gemv

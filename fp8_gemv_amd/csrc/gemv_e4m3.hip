@@ -101,6 +101,11 @@ struct Cfg {
   static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = K * THREADS * 16;
+  // the template arguments, for config_text
+  static constexpr const char *NAME = "Cfg";
+  static constexpr int P0 = WAVES_, P1 = RPW_, P2 = U_, P3 = K_, P4 = KD_, P6 = WPE_, P7 = SPLIT_,
+                       P8 = MT_;
+  static constexpr bool P5 = DB_;
 };
 
 template <bool BLK, class C>
@@ -356,21 +361,27 @@ static_assert(CfgSmall::SPLIT == CfgSmallB2::SPLIT && CfgSmall::SPLIT == CfgSmal
                   CfgSmall::SPLIT == CfgSmallB8::SPLIT && CfgMid::SPLIT == CfgMidB2::SPLIT,
               "one row split per in_f range");
 
+// The launch shape for (m, in_f): f is called with the Tag of the chosen configuration.
+template <class F>
+auto with_cfg(int m, int in_f, F &&f) {
+  if (in_f <= 8192) {
+    if (m == 1) return f(Tag<CfgSmall>{});
+    if (m == 2) return f(Tag<CfgSmallB2>{});
+    if (m <= 4) return f(Tag<CfgSmallB4>{});
+    return f(Tag<CfgSmallB8>{});
+  }
+  if (in_f <= 24576) return m == 1 ? f(Tag<CfgMid>{}) : f(Tag<CfgMidB2>{});
+  return f(Tag<CfgLarge>{});
+}
+
 template <bool BLK>
 hipError_t dispatch(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                     int grid_cols, const int8_t *qs, const float *d, float *y, int m, int in_f,
                     int out_f, hipStream_t s) {
-#define FP8GEMV_LAUNCH(CFG) \
-  launch_cfg<BLK, CFG>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s)
-  if (in_f <= 8192) {
-    if (m == 1) return FP8GEMV_LAUNCH(CfgSmall);
-    if (m == 2) return FP8GEMV_LAUNCH(CfgSmallB2);
-    if (m <= 4) return FP8GEMV_LAUNCH(CfgSmallB4);
-    return FP8GEMV_LAUNCH(CfgSmallB8);
-  }
-  if (in_f <= 24576) return m == 1 ? FP8GEMV_LAUNCH(CfgMid) : FP8GEMV_LAUNCH(CfgMidB2);
-  return FP8GEMV_LAUNCH(CfgLarge);
-#undef FP8GEMV_LAUNCH
+  return with_cfg(m, in_f, [&](auto tag) {
+    using C = typename decltype(tag)::type;
+    return launch_cfg<BLK, C>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+  });
 }
 
 }  // namespace
@@ -380,6 +391,20 @@ hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, co
                             float *y, int m, int in_f, int out_f, hipStream_t s) {
   if (blk128) return dispatch<true>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
   return dispatch<false>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+}
+
+LaunchDesc describe_gemv_e4m3(bool blk128, int m, int in_f, int out_f) {
+  return with_cfg(m, in_f, [&](auto tag) {
+    using C = typename decltype(tag)::type;
+    LaunchDesc r;
+    r.grid_x = (unsigned)((out_f + C::ROWS - 1) / C::ROWS);
+    r.grid_y = (unsigned)((m + C::MT - 1) / C::MT);
+    r.threads = C::THREADS;
+    r.lds = (unsigned)(C::MT * act_lds_bytes(in_f) + kSinkBytes);
+    r.kernel = blk128 ? "k_gemv_e4m3<true" : "k_gemv_e4m3<false";
+    r.config = config_text<C>();
+    return r;
+  });
 }
 
 }  // namespace fp8gemv

@@ -79,6 +79,11 @@ struct QCfg {
   static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = KQ * THREADS * 32;
+  // the template arguments, for config_text
+  static constexpr const char *NAME = "QCfg";
+  static constexpr int P0 = WAVES_, P1 = RPW_, P2 = U_, P3 = KQ_, P4 = KD_, P6 = WPE_,
+                       P7 = SPLIT_, P8 = MT_;
+  static constexpr bool P5 = DB_;
 };
 
 // LDS layout of the fast path: shaped activation (whole windows), then d_a padded with zeros
@@ -463,27 +468,61 @@ static_assert(QSmall::SPLIT == QSmallB2::SPLIT && QSmall::SPLIT == QSmallB4::SPL
 
 }  // namespace
 
+namespace {
+// The launch shape for (m, in_f) on the fast path: f is called with the Tag of the chosen
+// configuration.
+template <class F>
+auto with_cfg(int m, int in_f, F &&f) {
+  if (in_f <= 8192) {
+    if (m == 1) return f(Tag<QSmall>{});
+    if (m == 2) return f(Tag<QSmallB2>{});
+    if (m <= 4) return f(Tag<QSmallB4>{});
+    return f(Tag<QSmallB8>{});
+  }
+  if (in_f <= 24576) return m == 1 ? f(Tag<QMid>{}) : f(Tag<QMidB2>{});
+  return f(Tag<QLarge>{});
+}
+
+bool fast_path(const uint8_t *W, int64_t row_bytes, int in_f) {
+  return (in_f % 256 == 0) && (row_bytes % 16 == 0) &&
+         ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
+}
+}  // namespace
+
 hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
                             const float *d, float *y, int m, int in_f, int out_f, hipStream_t s) {
-  const bool fast = (in_f % 256 == 0) && (row_bytes % 16 == 0) &&
-                    ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
-  if (fast) {
-    if (in_f <= 8192) {
-      if (m == 1) return launch_fast<QSmall>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
-      if (m == 2) return launch_fast<QSmallB2>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
-      if (m <= 4) return launch_fast<QSmallB4>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
-      return launch_fast<QSmallB8>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
-    }
-    if (in_f <= 24576) {
-      if (m == 1) return launch_fast<QMid>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
-      return launch_fast<QMidB2>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
-    }
-    return launch_fast<QLarge>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+  if (fast_path(W, row_bytes, in_f)) {
+    return with_cfg(m, in_f, [&](auto tag) {
+      using C = typename decltype(tag)::type;
+      return launch_fast<C>(W, row_bytes, qs, d, y, m, in_f, out_f, s);
+    });
   }
   const dim3 g((out_f + kWaves - 1) / kWaves, m);
   hipLaunchKernelGGL(k_gemv_q8_0_generic, g, dim3(kThreads), 0, s, W, row_bytes, qs, d, y, in_f,
                      out_f);
   return hipGetLastError();
+}
+
+LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f) {
+  if (fast_path(W, row_bytes, in_f)) {
+    return with_cfg(m, in_f, [&](auto tag) {
+      using C = typename decltype(tag)::type;
+      LaunchDesc r;
+      r.grid_x = (unsigned)((out_f + C::ROWS - 1) / C::ROWS);
+      r.grid_y = (unsigned)((m + C::MT - 1) / C::MT);
+      r.threads = C::THREADS;
+      r.lds = (unsigned)fast_lds_bytes(in_f, C::MT);
+      r.kernel = "k_gemv_q8_0_fast";
+      r.config = config_text<C>();
+      return r;
+    });
+  }
+  LaunchDesc r;
+  r.grid_x = (unsigned)((out_f + kWaves - 1) / kWaves);
+  r.grid_y = (unsigned)m;
+  r.threads = kThreads;
+  r.kernel = "k_gemv_q8_0_generic";
+  return r;
 }
 
 }  // namespace fp8gemv

@@ -199,14 +199,82 @@ int requant_e4m3_blk128_q8_0(const uint8_t *W, int64_t row_bytes, const float *g
 /*
  * fp8gemv_read_bytes -- measurement aid, not a step of the matvec: streams `bytes` bytes from
  * p with the GEMVs' load pattern (16-byte non-temporal loads, 1 KiB per wave-wide load,
- * 8 KiB per wave) and discards them; `sink` (one uint32) is written only in the
- * practically impossible case that the folded data equal a fixed constant.  Timing it on a
- * cold range gives the achievable read ceiling the GEMV timings are compared with.
+ * 8 KiB per wave, 4-wave workgroups) and discards them; `sink` (one uint32) is written only in
+ * the practically impossible case that the folded data equal a fixed constant.  Timing it on
+ * a cold range gives the achievable read ceiling the GEMV timings are compared with.  The
+ * same as fp8gemv_read_pattern with FP8GEMV_READ_CHUNK8K.
  *   p      device pointer, 16-byte aligned;  1 <= bytes <= FP8GEMV_MAX_READ_BYTES
  *   sink   device pointer to one uint32, 4-byte aligned
  */
-#define FP8GEMV_MAX_READ_BYTES ((int64_t)1 << 40)
+#define FP8GEMV_MAX_READ_BYTES ((int64_t)1 << 35)
 int fp8gemv_read_bytes(const void *p, int64_t bytes, uint32_t *sink, void *stream);
+
+/*
+ * fp8gemv_read_pattern -- measurement aid: the same kind of discarding stream in one of several
+ * load patterns, so that the read ceiling is not only the GEMVs' own pattern measured against
+ * itself, and so that a launch's fixed cost can be taken apart.  Source of the discipline:
+ * gemv_e4m3_bench.rs, DRAM-COLD DISCIPLINE (times are only meaningful on weights that come from
+ * DRAM, not from the last-level cache).  Patterns:
+ *   FP8GEMV_READ_CHUNK8K     4-wave workgroups, 8 KiB contiguous per wave (8 loads in flight
+ *                            per lane), one workgroup per 32 KiB (= fp8gemv_read_bytes)
+ *   FP8GEMV_READ_CHUNK16K    as CHUNK8K with 16 KiB per wave (16 loads in flight per lane)
+ *   FP8GEMV_READ_WG8         8-wave workgroups, 8 KiB per wave
+ *   FP8GEMV_READ_WG16        16-wave workgroups, 8 KiB per wave
+ *   FP8GEMV_READ_PERSISTENT  a grid of the device's resident waves (8 four-wave workgroups
+ *                            per compute unit); each wave strides over 4 KiB blocks with the
+ *                            next block in flight while the current one is folded
+ *   FP8GEMV_READ_CACHED      as CHUNK8K without the non-temporal hint
+ *   FP8GEMV_READ_ROWS_1K     rows of row_bytes, one wave per row, 1 KiB windows in batches
+ *                            of 4 with the next batch in flight (the e4m3 GEMV's m = 1 pattern)
+ *   FP8GEMV_READ_ROWS_816    the same with 816-byte windows read by 51 lanes (the Q8_0 GEMV's
+ *                            pattern: three 272-byte groups of eight 34-byte blocks)
+ *   FP8GEMV_READ_EMPTY       CHUNK8K's grid with no loads: dispatch and drain alone
+ *   FP8GEMV_READ_ONE_WAVE    one wave loads the first min(bytes, 1 KiB): a launch plus one cold
+ *                            round trip to HBM
+ *   p, bytes, sink   as for fp8gemv_read_bytes
+ *   row_bytes        ROWS_* patterns only: 1024 <= row_bytes <= 2^20, a multiple of 16, and
+ *                    bytes a multiple of it; ignored by the other patterns
+ * Returns FP8GEMV_ERR_SHAPE for an unknown pattern or a bad row_bytes.
+ */
+#define FP8GEMV_READ_CHUNK8K     0
+#define FP8GEMV_READ_CHUNK16K    1
+#define FP8GEMV_READ_WG8         2
+#define FP8GEMV_READ_WG16        3
+#define FP8GEMV_READ_PERSISTENT  4
+#define FP8GEMV_READ_CACHED      5
+#define FP8GEMV_READ_ROWS_1K     6
+#define FP8GEMV_READ_ROWS_816    7
+#define FP8GEMV_READ_EMPTY       8
+#define FP8GEMV_READ_ONE_WAVE    9
+#define FP8GEMV_READ_NUM_PATTERNS 10
+int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_bytes,
+                         uint32_t *sink, void *stream);
+
+/*
+ * fp8gemv_gemv_launch_info -- what one GEMV call with these arguments would launch, without
+ * launching it: for profilers and benches that label kernel traces.  The library's own launch
+ * selection fills it in, so it always agrees with the launch.
+ *   container   FP8GEMV_Q8_0, FP8GEMV_E4M3 or FP8GEMV_E4M3_BLK128
+ *   W, row_bytes, m, in_f, out_f   as for that container's GEMV; W is never dereferenced (only
+ *               its alignment matters, for the Q8_0 fast-path choice)
+ *   info        out: grid in workgroups (x = weight rows, y = activation-row passes), threads per
+ *               workgroup, dynamic LDS bytes, the kernel family and its launch configuration as
+ *               they appear in the demangled kernel symbol (static strings)
+ * Returns the argument checks of the GEMV (FP8GEMV_ERR_* as above, W and info must be
+ * non-NULL) and FP8GEMV_ERR_SHAPE for an unknown container; touches no device.
+ */
+#define FP8GEMV_Q8_0         0
+#define FP8GEMV_E4M3         1
+#define FP8GEMV_E4M3_BLK128  2
+typedef struct {
+  uint32_t grid_x, grid_y;
+  uint32_t workgroup_size;
+  uint32_t lds_bytes;
+  const char *kernel;
+  const char *config;
+} fp8gemv_launch_info;
+int fp8gemv_gemv_launch_info(int container, const void *W, int64_t row_bytes, int m, int in_f,
+                             int out_f, fp8gemv_launch_info *info);
 
 /* Human-readable text for a return code (static storage, never NULL). */
 const char *fp8gemv_strerror(int rc);

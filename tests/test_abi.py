@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                                   "silu_mul_f32", "silu_mul_q8_1",
                                   "gemv_q8_0_q81", "gemv_e4m3_q81", "gemv_e4m3_blk128_q81",
                                   "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
-                                  "fp8gemv_read_bytes", "fp8gemv_strerror"])
+                                  "fp8gemv_read_bytes", "fp8gemv_read_pattern",
+                                  "fp8gemv_gemv_launch_info", "fp8gemv_strerror"])
 
 
 def test_library_exports_every_declared_symbol(fg):
@@ -157,7 +158,51 @@ def test_read_bytes_argument_errors(fg):
     assert L.fp8gemv_read_bytes(None, 1024, FAKE, None) == fg.FP8GEMV_ERR_NULL
     assert L.fp8gemv_read_bytes(FAKE, 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
     assert L.fp8gemv_read_bytes(FAKE + 4, 1024, FAKE, None) == fg.FP8GEMV_ERR_ALIGN
-    assert L.fp8gemv_read_bytes(FAKE, (1 << 40) + 1, FAKE, None) == fg.FP8GEMV_ERR_TOO_LARGE
+    assert L.fp8gemv_read_bytes(FAKE, (1 << 35) + 1, FAKE, None) == fg.FP8GEMV_ERR_TOO_LARGE
+
+
+def test_launch_info_argument_errors_and_agreement(fg):
+    import ctypes
+    L = fg.lib()
+    info = fg.LaunchInfo()
+    ref = ctypes.byref(info)
+    assert L.fp8gemv_gemv_launch_info(0, None, 5440, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_NULL
+    assert L.fp8gemv_gemv_launch_info(0, FAKE, 5440, 1, 5120, 10, None) == fg.FP8GEMV_ERR_NULL
+    assert L.fp8gemv_gemv_launch_info(3, FAKE, 5440, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_SHAPE
+    assert L.fp8gemv_gemv_launch_info(0, FAKE, 5440, 0, 5120, 10, ref) == fg.FP8GEMV_ERR_SHAPE
+    assert L.fp8gemv_gemv_launch_info(1, FAKE, 5120, 1, 5100, 10, ref) == fg.FP8GEMV_ERR_SHAPE
+    assert L.fp8gemv_gemv_launch_info(0, FAKE, 5438, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_ROW_BYTES
+    assert L.fp8gemv_gemv_launch_info(1, FAKE + 8, 5120, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_ALIGN
+    # every row is covered once per activation-row pass; a misaligned Q8_0 plane takes the
+    # generic kernel
+    for c in ("q8_0", "e4m3", "blk128"):
+        for m in (1, 2, 3, 5, 8, 11):
+            for in_f in (5120, 17408, 32768):
+                rb = in_f // 32 * 34 if c == "q8_0" else in_f
+                i = fg.gemv_launch_info(c, rb, m, in_f, 17408)
+                assert i["grid_x"] >= 1 and i["grid_y"] >= 1 and i["workgroup_size"] % 64 == 0
+                assert i["kernel"].startswith("k_gemv_") and "Cfg<" in i["config"]
+    g = fg.gemv_launch_info("q8_0", 5440, 1, 5120, 100, w_align=2)
+    assert g["kernel"] == "k_gemv_q8_0_generic" and g["config"] == ""
+
+
+def test_read_pattern_argument_errors(fg):
+    L = fg.lib()
+    P = fg.READ_PATTERNS
+    assert len(P) == fg.FP8GEMV_READ_NUM_PATTERNS
+    assert L.fp8gemv_read_pattern(None, 1024, 0, 0, FAKE, None) == fg.FP8GEMV_ERR_NULL
+    assert L.fp8gemv_read_pattern(FAKE, 1024, 0, 0, None, None) == fg.FP8GEMV_ERR_NULL
+    assert L.fp8gemv_read_pattern(FAKE, 0, 0, 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.fp8gemv_read_pattern(FAKE, 1024, -1, 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
+    assert L.fp8gemv_read_pattern(FAKE, 1024, len(P), 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
+    for rows in ("rows_1k", "rows_816"):
+        for rb, nbytes in ((0, 4096), (1008, 4032), (1040, 4096), (1024 + 8, 2064),
+                           ((1 << 20) + 16, (1 << 20) + 16)):
+            assert L.fp8gemv_read_pattern(FAKE, nbytes, P[rows], rb, FAKE,
+                                          None) == fg.FP8GEMV_ERR_SHAPE, (rows, rb, nbytes)
+    assert L.fp8gemv_read_pattern(FAKE, (1 << 35) + 1, 0, 0, FAKE, None) == fg.FP8GEMV_ERR_TOO_LARGE
+    assert L.fp8gemv_read_pattern(FAKE + 4, 1024, 0, 0, FAKE, None) == fg.FP8GEMV_ERR_ALIGN
+    assert L.fp8gemv_read_pattern(FAKE, 1024, 0, 0, FAKE + 2, None) == fg.FP8GEMV_ERR_ALIGN
 
 
 def test_binding_rejects_cpu_tensors_and_short_buffers(fg):

@@ -352,6 +352,25 @@ def test_read_bytes_measurement_kernel_runs(fg):
     assert int(host(sink)[0]) == 7
 
 
+@pytest.mark.parametrize("pattern", ["chunk8k", "chunk16k", "wg8", "wg16", "persistent",
+                                     "cached", "rows_1k", "rows_816", "empty", "one_wave"])
+def test_read_patterns_run(fg, pattern):
+    # Every measurement pattern over ragged and whole ranges; the rows patterns over rows of
+    # 5120 and 5440 bytes (the e4m3 and Q8_0 rows at in_f = 5120).  Nothing is computed, so
+    # the check is that each launch completes and leaves the sink alone.
+    case(f"fp8gemv_read_pattern {pattern}")
+    buf = torch.randint(0, 255, (64 * 5440,), dtype=torch.uint8, device=dev())
+    sink = torch.full((1,), 7, dtype=torch.int32, device=dev())
+    if pattern.startswith("rows"):
+        for rb in (5120, 5440):
+            for rows in (1, 5, 64):
+                fg.fp8gemv_read_pattern(buf, rows * rb, pattern, sink, row_bytes=rb)
+    else:
+        for nbytes in (16, 1000 * 16, 33 * 1024 + 48, buf.numel()):
+            fg.fp8gemv_read_pattern(buf, nbytes, pattern, sink)
+    assert int(host(sink)[0]) == 7
+
+
 def test_calls_on_an_explicit_stream_are_ordered_on_it(fg):
     # Every entry point takes the caller's stream: a producer -> GEMV chain issued on a
     # non-default stream runs there in order and matches the same chain on the default one.
