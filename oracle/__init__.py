@@ -17,6 +17,10 @@ What it computes (docs.rs pages of memra-engine 0.125.0):
   and THE BLOCK-128 ARM), f64 terms and sums -- see ``oracle.c``.
 * The SiLU-gated producer silu(gate) * up -> q8_1 (gate page, ``main``: the MoE expert-ff
   site), in f64 with one rounding to f32, then the q8_1 step -- see ``oracle.c``.
+* The KDA gated-norm producer the gate page names at the 64-head x 128 KDA width (``main``):
+  per head, RMSNorm over the head's head_dim values times a shared gain, times the sigmoid
+  output gate, in f64 with one rounding to f32, then the q8_1 step.  The page gives no
+  formula; the reading is restated next to ``gated_rms_norm``.
 * The load-time e4m3 -> Q8_0 requantisation the same page names as its ship path (QUESTION),
   in f32 with an fp16 block scale -- see ``oracle.c`` for the reading it takes.
 
@@ -137,6 +141,47 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float = EPS):
         s64[r] = s
         z64[r] = (x64[r] * w64) * s
     return z64, z64.astype(np.float32), s64
+
+
+def gated_rms_norm(o: np.ndarray, g: np.ndarray, w: np.ndarray, head_dim: int,
+                   eps: float = EPS):
+    """KDA gated-norm of f32 rows o [nrows, ncols] with output gate g [nrows, ncols] and gain
+    w [head_dim] (shared by all heads), ncols = heads * head_dim.
+
+    The gate page (q8_fuse_gate.rs, module doc and ``main``) names the KDA gated-norm site at
+    the KDA qkv width, 64 heads x 128 head_dim = 8192, as a producer site still on the unfused
+    chain, but gives no formula.  Reading taken: the output stage of a KDA (Kimi delta
+    attention) layer -- RMSNorm over each head's head_dim values (not over the whole row), the
+    gain indexed by the position inside the head, then the sigmoid output gate applied after
+    the norm, element by element.  eps is the f32 1e-6 the page passes to rms_norm, widened.
+    For head h of row r, with j over that head's columns, all in f64:
+      ss_h = sum_j o_j^2 (exactly rounded, math.fsum),  s_h = 1 / sqrt(ss_h / head_dim + eps)
+      z64_j = ((o_j * w_{j mod head_dim}) * s_h) * (1 / (1 + exp(-g_j)))
+    and the stored f32 is z32 = float32(z64).  Returns (z64, z32)."""
+    o = np.atleast_2d(_c(o, np.float32))
+    g = np.atleast_2d(_c(g, np.float32))
+    w = _c(w, np.float32)
+    nrows, ncols = o.shape
+    assert g.shape == o.shape and w.shape == (head_dim,) and ncols % head_dim == 0
+    eps64 = float(np.float32(eps))
+    o64, g64, w64 = o.astype(np.float64), g.astype(np.float64), w.astype(np.float64)
+    z64 = np.empty((nrows, ncols), dtype=np.float64)
+    for r in range(nrows):
+        for h in range(ncols // head_dim):
+            sl = slice(h * head_dim, (h + 1) * head_dim)
+            ss = math.fsum(o64[r, sl] * o64[r, sl])
+            s = 1.0 / math.sqrt(ss / head_dim + eps64)
+            gate = np.array([1.0 / (1.0 + math.exp(-v)) for v in g64[r, sl]])
+            z64[r, sl] = ((o64[r, sl] * w64) * s) * gate
+    return z64, z64.astype(np.float32)
+
+
+def gated_rmsnorm_q8_1(o: np.ndarray, g: np.ndarray, w: np.ndarray, head_dim: int,
+                       eps: float = EPS):
+    """The KDA gated-norm producer: gated_rms_norm then q8_1 of its f32 output."""
+    z64, z32 = gated_rms_norm(o, g, w, head_dim, eps)
+    qs, d = quantize_q8_1(z32)
+    return {"z64": z64, "z32": z32, "qs": qs, "d": d}
 
 
 def quantize_q8_1(z: np.ndarray):

@@ -519,3 +519,99 @@ def test_silu_odd_part_identity_and_scaling():
     h1, _ = oracle.silu_mul(g, u)
     h2, _ = oracle.silu_mul(g, 2 * u)  # doubling is exact in f32 and f64
     assert np.array_equal(h2, 2 * h1)
+
+
+# ------------------------------------------------------------ KDA gated-norm producer
+# The gate page names the KDA gated-norm site (64 heads x 128 head_dim = 8192) without a
+# formula; the oracle reads it as per-head RMSNorm x gain x sigmoid(gate), in f64.  Pinned by
+# torch (rms_norm over each head reshaped as its own row, times torch.sigmoid), a 50-digit
+# Decimal evaluation, the saturated and zero gates (exact reductions to the plain per-head
+# RMSNorm and its half), head independence and the sigmoid's symmetry.
+
+def _gated_inputs(ncols, head_dim, nrows=2, seed=21):
+    o = np.stack([synth.f32(seed + r, ncols) for r in range(nrows)])
+    g = np.stack([synth.f32(seed + 100 + r, ncols) for r in range(nrows)])
+    return o, g, synth.gain(head_dim)
+
+
+@pytest.mark.parametrize("head_dim", [32, 64, 128, 256])
+def test_gated_norm_against_torch_f64(head_dim):
+    o, g, w = _gated_inputs(8192, head_dim)
+    z64, z32 = oracle.gated_rms_norm(o, g, w, head_dim)
+    ot = torch.from_numpy(o).double().reshape(2, -1, head_dim)
+    ref = (torch.nn.functional.rms_norm(ot, (head_dim,), weight=torch.from_numpy(w).double(),
+                                        eps=EPS32).reshape(2, -1)
+           * torch.sigmoid(torch.from_numpy(g).double())).numpy()
+    assert np.all(np.abs(z64 - ref) <= 1e-14 * np.abs(ref) + 1e-300)
+    assert np.array_equal(z32, z64.astype(np.float32))
+
+
+def test_gated_norm_saturated_and_zero_gate():
+    # g = 40: 1 + exp(-40) rounds to 1 in f64, so the gate is exactly 1 and every head is the
+    # plain RMSNorm of its own 128 values (torch's rms_norm on that slice as a row).  g = 0:
+    # the gate is exactly 1/2, so z is exactly half of that.
+    head_dim = 128
+    o, _, w = _gated_inputs(1024, head_dim)
+    z_one, _ = oracle.gated_rms_norm(o, np.full_like(o, 40.0), w, head_dim)
+    z_half, _ = oracle.gated_rms_norm(o, np.zeros_like(o), w, head_dim)
+    assert np.array_equal(z_half, 0.5 * z_one)
+    for r in range(2):
+        for h in range(1024 // head_dim):
+            sl = slice(h * head_dim, (h + 1) * head_dim)
+            ref = torch.nn.functional.rms_norm(torch.from_numpy(o[r, sl]).double(), (head_dim,),
+                                               weight=torch.from_numpy(w).double(),
+                                               eps=EPS32).numpy()
+            assert np.all(np.abs(z_one[r, sl] - ref) <= 1e-14 * np.abs(ref))
+    # a whole-row norm would differ: the heads' mean squares are not all equal
+    whole = torch.nn.functional.rms_norm(torch.from_numpy(o).double(), (1024,),
+                                         weight=torch.from_numpy(np.tile(w, 8)).double(),
+                                         eps=EPS32).numpy()
+    assert np.max(np.abs(whole - z_one) / np.abs(whole)) > 1e-3
+
+
+@pytest.mark.parametrize("c", [2.0 ** -10, 0.75, -3.5])
+def test_gated_norm_constant_head_closed_form(c):
+    # o = c over the head, w = 1, g = 0: z = (c / sqrt(c^2 + eps)) / 2
+    head_dim = 64
+    o = np.full((1, 2 * head_dim), c, dtype=np.float32)
+    z64, _ = oracle.gated_rms_norm(o, np.zeros_like(o), np.ones(head_dim, np.float32), head_dim)
+    getcontext().prec = 50
+    dc = Decimal(c)
+    want = float(dc / (dc * dc + Decimal(EPS32)).sqrt() / 2)
+    assert np.all(np.abs(z64 - want) <= 4e-16 * abs(want))
+
+
+def test_gated_norm_decimal_reference():
+    getcontext().prec = 50
+    head_dim = 128
+    o, g, w = _gated_inputs(2 * head_dim, head_dim, nrows=1, seed=31)
+    z64, _ = oracle.gated_rms_norm(o, g, w, head_dim)
+    for h in range(2):
+        sl = range(h * head_dim, (h + 1) * head_dim)
+        ss = sum(Decimal(float(o[0, j])) ** 2 for j in sl)
+        s = 1 / (ss / head_dim + Decimal(EPS32)).sqrt()
+        for j in sl:
+            gd = Decimal(float(g[0, j]))
+            want = Decimal(float(o[0, j])) * Decimal(float(w[j % head_dim])) * s / (1 + (-gd).exp())
+            assert abs(Decimal(float(z64[0, j])) - want) <= abs(want) * Decimal(2) ** -50, j
+
+
+def test_gated_norm_heads_independent_and_gate_symmetry():
+    head_dim = 128
+    o, g, w = _gated_inputs(1024, head_dim)
+    z64, _ = oracle.gated_rms_norm(o, g, w, head_dim)
+    # changing head 3 leaves every other head's output unchanged
+    o2 = o.copy()
+    o2[:, 3 * head_dim:4 * head_dim] *= np.float32(3.0)
+    z2, _ = oracle.gated_rms_norm(o2, g, w, head_dim)
+    keep = np.ones(1024, bool)
+    keep[3 * head_dim:4 * head_dim] = False
+    assert np.array_equal(z2[:, keep], z64[:, keep])
+    # permuting whole heads permutes the output
+    perm = np.concatenate([np.arange(h * head_dim, (h + 1) * head_dim) for h in (5, 0, 7, 2, 1, 6, 4, 3)])
+    zp, _ = oracle.gated_rms_norm(o[:, perm], g[:, perm], w, head_dim)
+    assert np.array_equal(zp, z64[:, perm])
+    # sigmoid(g) + sigmoid(-g) = 1
+    zn, _ = oracle.gated_rms_norm(o, -g, w, head_dim)
+    z1, _ = oracle.gated_rms_norm(o, np.full_like(g, 40.0), w, head_dim)
+    assert np.allclose(z64 + zn, z1, rtol=1e-14, atol=1e-15)
