@@ -845,6 +845,28 @@ def main() -> int:
             g.replay()
             prod_us[f"silu_{variant}@{ncols}"] = round(timed(g.replay, 50) * 1e3, 3)
 
+    # KDA gated-norm producer at the page's KDA width (64 heads x 128 head_dim = 8192), fused
+    # vs two-launch chain.
+    if not args.kernels_only:
+        ncols, hd = 8192, 128
+        ot = torch.from_numpy(synth.f32(0x0DA0 ^ ncols, ncols)).to(dev)
+        gt = torch.from_numpy(synth.f32(0x6A7E ^ ncols, ncols)).to(dev)
+        wt = torch.from_numpy(synth.gain(hd)).to(dev)
+        zt = torch.empty(ncols, device=dev)
+        qs = torch.empty(ncols, dtype=torch.int8, device=dev)
+        d = torch.empty(ncols // 32, device=dev)
+        for variant in ("fused", "chain"):
+            def run():
+                if variant == "fused":
+                    fg.gated_rmsnorm_q8_1(ot, gt, wt, zt, qs, d, ncols, hd, 1, EPS)
+                else:
+                    fg.gated_rms_norm_f32(ot, gt, wt, zt, ncols, hd, 1, EPS)
+                    fg.quantize_q8_1(zt, qs, d, 1, ncols)
+            run()
+            g = capture(lambda: [run() for _ in range(50)])
+            g.replay()
+            prod_us[f"kda_gated_{variant}@{ncols}"] = round(timed(g.replay, 50) * 1e3, 3)
+
     # DRAM-cold cross-checks on the 17408x5120 e4m3 launch (gemv_e4m3_bench.rs, DRAM-COLD
     # DISCIPLINE): (a) per-launch time with 512 MB pushed through the device right before each
     # launch must match the rotation's; (b) the time over a growing number of rotated copies

@@ -31,6 +31,7 @@ FP8GEMV_MAX_IN_F = 65536
 FP8GEMV_MAX_M = 65535
 
 EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "silu_mul_f32", "silu_mul_q8_1",
+           "gated_rms_norm_f32", "gated_rmsnorm_q8_1",
            "gemv_q8_0_q81", "gemv_e4m3_q81",
            "gemv_e4m3_blk128_q81", "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
            "fp8gemv_read_bytes", "fp8gemv_read_pattern", "fp8gemv_gemv_launch_info",
@@ -71,6 +72,8 @@ def _load() -> ctypes.CDLL:
         "rmsnorm_q8_1": [vp, vp, vp, vp, vp, i32, i32, f32, vp],
         "silu_mul_f32": [vp, vp, vp, i32, i32, vp],
         "silu_mul_q8_1": [vp, vp, vp, vp, vp, i32, i32, vp],
+        "gated_rms_norm_f32": [vp, vp, vp, vp, i32, i32, i32, f32, vp],
+        "gated_rmsnorm_q8_1": [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp],
         "gemv_q8_0_q81": [vp, i64, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_q81": [vp, i64, f32, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_blk128_q81": [vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, vp],
@@ -210,6 +213,34 @@ def silu_mul_q8_1(gate, up, h, qs, d, ncols: int, nrows: int, stream=None) -> No
          _ptr(qs, "qs", torch.int8, n, dev),
          _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
          ncols, nrows, _stream(stream, dev))
+
+
+def gated_rms_norm_f32(o, g, w, z, ncols: int, head_dim: int, nrows: int, eps: float = 1e-6,
+                       stream=None) -> None:
+    """KDA gated norm z = RMSNorm per head(o) * w * sigmoid(g) (first half of its chain)."""
+    dev = _dev(o)
+    n = ncols * nrows
+    _run("gated_rms_norm_f32", dev,
+         _ptr(o, "o", torch.float32, n, dev),
+         _ptr(g, "g", torch.float32, n, dev),
+         _ptr(w, "w", torch.float32, head_dim, dev),
+         _ptr(z, "z", torch.float32, n, dev),
+         ncols, head_dim, nrows, eps, _stream(stream, dev))
+
+
+def gated_rmsnorm_q8_1(o, g, w, z, qs, d, ncols: int, head_dim: int, nrows: int,
+                       eps: float = 1e-6, stream=None) -> None:
+    """Fused KDA gated-norm producer: the gated norm then q8_1 in one launch (z may be None)."""
+    dev = _dev(o)
+    n = ncols * nrows
+    _run("gated_rmsnorm_q8_1", dev,
+         _ptr(o, "o", torch.float32, n, dev),
+         _ptr(g, "g", torch.float32, n, dev),
+         _ptr(w, "w", torch.float32, head_dim, dev),
+         _ptr(z, "z", torch.float32, n, dev),
+         _ptr(qs, "qs", torch.int8, n, dev),
+         _ptr(d, "d", torch.float32, (ncols // 32) * nrows, dev),
+         ncols, head_dim, nrows, eps, _stream(stream, dev))
 
 
 # -------------------------------------------------------------------------------- GEMVs

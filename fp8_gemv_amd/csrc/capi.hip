@@ -74,6 +74,39 @@ int silu_mul_q8_1(const float *gate, const float *up, float *h, int8_t *qs, floa
       fp8gemv::launch_silu_mul_q8_1(gate, up, h, qs, d, ncols, nrows, (hipStream_t)stream));
 }
 
+namespace {
+int check_gated(const float *o, const float *g, const float *w, int ncols, int head_dim,
+                int nrows) {
+  if (!o || !g || !w) return FP8GEMV_ERR_NULL;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return FP8GEMV_ERR_SHAPE;
+  if (nrows < 1 || bad_cols(ncols) || ncols % head_dim != 0) return FP8GEMV_ERR_SHAPE;
+  if (ncols > FP8GEMV_MAX_IN_F || nrows > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
+  if (!aligned(o, 16) || !aligned(g, 16) || !aligned(w, 16)) return FP8GEMV_ERR_ALIGN;
+  return FP8GEMV_OK;
+}
+}  // namespace
+
+int gated_rms_norm_f32(const float *o, const float *g, const float *w, float *z, int ncols,
+                       int head_dim, int nrows, float eps, void *stream) {
+  if (!z) return FP8GEMV_ERR_NULL;
+  const int rc = check_gated(o, g, w, ncols, head_dim, nrows);
+  if (rc) return rc;
+  if (!aligned(z, 16)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_gated_rms_norm(o, g, w, z, ncols, head_dim, nrows, eps,
+                                                  (hipStream_t)stream));
+}
+
+int gated_rmsnorm_q8_1(const float *o, const float *g, const float *w, float *z, int8_t *qs,
+                       float *d, int ncols, int head_dim, int nrows, float eps, void *stream) {
+  if (!qs || !d) return FP8GEMV_ERR_NULL;
+  const int rc = check_gated(o, g, w, ncols, head_dim, nrows);
+  if (rc) return rc;
+  if ((z && !aligned(z, 16)) || !aligned(qs, 16) || !aligned(d, 4)) return FP8GEMV_ERR_ALIGN;
+  return launch_rc(fp8gemv::launch_gated_rmsnorm_q8_1(o, g, w, z, qs, d, ncols, head_dim, nrows,
+                                                      eps, (hipStream_t)stream));
+}
+
 int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
                   int m, int in_f, int out_f, void *stream) {
   const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);

@@ -137,6 +137,11 @@ hipError_t launch_rmsnorm_q8_1(const float *x, const float *w, float *z, int8_t 
                                int ncols, int nrows, float eps, hipStream_t s);
 hipError_t launch_silu_mul(const float *g, const float *u, float *h, int ncols, int nrows,
                            hipStream_t s);
+hipError_t launch_gated_rms_norm(const float *o, const float *g, const float *w, float *z,
+                                 int ncols, int head_dim, int nrows, float eps, hipStream_t s);
+hipError_t launch_gated_rmsnorm_q8_1(const float *o, const float *g, const float *w, float *z,
+                                     int8_t *qs, float *d, int ncols, int head_dim, int nrows,
+                                     float eps, hipStream_t s);
 hipError_t launch_silu_mul_q8_1(const float *g, const float *u, float *h, int8_t *qs, float *d,
                                 int ncols, int nrows, hipStream_t s);
 hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,

@@ -25,6 +25,18 @@
 // pattern: a chain (silu_mul_f32 then quantize_q8_1) and a fused kernel sharing the device
 // function h_value, byte-identical by construction.  h_value in f64, rounded once to f32:
 //   h_j = (float)((g_j / (1 + exp(-g_j))) * u_j)            (g, u widened exactly to f64)
+//
+// The third front end, the KDA gated norm (the same page names the KDA gated-norm site at the
+// KDA qkv width, 64 heads x 128 head_dim, as still on the unfused chain; no formula is given,
+// the rule is the output stage of a Kimi-delta-attention layer): per head of head_dim
+// columns, the RMS factor of that head only, the gain indexed inside the head, then the
+// sigmoid output gate, in f64 with one rounding to f32:
+//   s_h = 1 / sqrt(sum_{j in h} o_j^2 / head_dim + eps)     (double-double sum, as above)
+//   z_j = (float)((((double)o_j * w_{j mod head_dim}) * s_h) * (1 / (1 + exp(-g_j))))
+// A head is head_dim / 4 consecutive lanes; its sum of squares is formed per quad by DPP
+// (identical bits in all four lanes) and then over the head's quads in quad order from
+// uniform lane reads.  Chain (gated_rms_norm_f32 then quantize_q8_1) and fused kernel call
+// the same device functions, so they are byte-identical by construction.
 #include "common.hpp"
 
 namespace fp8gemv {
@@ -157,6 +169,102 @@ __device__ __forceinline__ uint32_t quant_group(const float z[4], float &d_out) 
   return packed;
 }
 
+// 1 / sqrt(mean over the head of o^2 + eps) for the head that holds this lane's 4 columns.
+// Heads are D / 4 consecutive lanes (D in {32, 64, 128, 256}, so a head never leaves its wave);
+// every lane of the wave must call this together.
+template <int D>
+__device__ double head_scale(const float o[4], float eps) {
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head_dim");
+  constexpr int kQuadsPerHead = D / 16;
+  constexpr int kHeadsPerWave = kWave * 4 / D;
+  double hi = 0.0, lo = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double p = (double)o[i] * (double)o[i];
+    double s, e;
+    two_sum(hi, p, s, e);
+    hi = s;
+    lo += e;
+  }
+  // quad sums: both operands of every step are the same two values in every lane of the
+  // quad (added in either order, TwoSum gives the same sum and the same exact error)
+  dd_add(hi, lo, dpp_f64<kQuadPerm1032>(hi), dpp_f64<kQuadPerm1032>(lo));
+  dd_add(hi, lo, dpp_f64<kQuadPerm2301>(hi), dpp_f64<kQuadPerm2301>(lo));
+  const int head = (int)(threadIdx.x % kWave) / (D / 4);
+  double shi = 0.0, slo = 0.0;
+#pragma unroll
+  for (int h = 0; h < kHeadsPerWave; ++h) {
+    double thi = lane_f64(hi, 4 * h * kQuadsPerHead), tlo = lane_f64(lo, 4 * h * kQuadsPerHead);
+#pragma unroll
+    for (int k = 1; k < kQuadsPerHead; ++k)
+      dd_add(thi, tlo, lane_f64(hi, 4 * (h * kQuadsPerHead + k)),
+             lane_f64(lo, 4 * (h * kQuadsPerHead + k)));
+    shi = head == h ? thi : shi;
+    slo = head == h ? tlo : slo;
+  }
+  const double ss = shi + slo;
+  return 1.0 / sqrt(ss / (double)D + (double)eps);
+}
+
+// Gated z of one column, in f64 with a single rounding to f32.
+__device__ __forceinline__ float gated_z(float o, float w, float g, double s) {
+  const double gate = 1.0 / (1.0 + exp(-(double)g));
+  return (float)((((double)o * (double)w) * s) * gate);
+}
+
+// This thread's 4 columns of the gated norm (zeros, and no loads, past ncols).
+template <int D>
+__device__ __forceinline__ void gated_columns(const float *__restrict__ o,
+                                              const float *__restrict__ g,
+                                              const float *__restrict__ w, int64_t row, int j,
+                                              int ncols, float eps, float z[4]) {
+  float ov[4] = {0.f, 0.f, 0.f, 0.f}, gv[4] = {0.f, 0.f, 0.f, 0.f}, wv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (j < ncols) {
+    const float4 a = *reinterpret_cast<const float4 *>(o + row * ncols + j);
+    const float4 b = *reinterpret_cast<const float4 *>(g + row * ncols + j);
+    const float4 c = *reinterpret_cast<const float4 *>(w + j % D);
+    ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
+    gv[0] = b.x; gv[1] = b.y; gv[2] = b.z; gv[3] = b.w;
+    wv[0] = c.x; wv[1] = c.y; wv[2] = c.z; wv[3] = c.w;
+  }
+  const double s = head_scale<D>(ov, eps);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = gated_z(ov[i], wv[i], gv[i], s);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_gated_rms_norm(const float *__restrict__ o,
+                                                             const float *__restrict__ g,
+                                                             const float *__restrict__ w,
+                                                             float *__restrict__ z, int ncols,
+                                                             float eps) {
+  const int64_t row = blockIdx.y;
+  const int j = blockIdx.x * kColsPerPass + threadIdx.x * 4;
+  float zv[4];
+  gated_columns<D>(o, g, w, row, j, ncols, eps, zv);
+  if (j < ncols)
+    *reinterpret_cast<float4 *>(z + row * ncols + j) = make_float4(zv[0], zv[1], zv[2], zv[3]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_gated_rmsnorm_q8_1(
+    const float *__restrict__ o, const float *__restrict__ g, const float *__restrict__ w,
+    float *__restrict__ z, int8_t *__restrict__ qs, float *__restrict__ d, int ncols, float eps) {
+  const int64_t row = blockIdx.y;
+  const int j = blockIdx.x * kColsPerPass + threadIdx.x * 4;
+  const bool live = j < ncols;  // whole 8-lane groups are live or not (ncols % 32 == 0)
+  float zv[4];
+  gated_columns<D>(o, g, w, row, j, ncols, eps, zv);
+  if (live && z != nullptr)
+    *reinterpret_cast<float4 *>(z + row * ncols + j) = make_float4(zv[0], zv[1], zv[2], zv[3]);
+  float db;
+  const uint32_t packed = quant_group(zv, db);
+  if (live) {
+    *reinterpret_cast<uint32_t *>(qs + row * ncols + j) = packed;
+    if ((threadIdx.x & 7) == 0) d[row * (ncols / 32) + j / 32] = db;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_rms_norm(const float *__restrict__ x,
                                                        const float *__restrict__ w,
                                                        float *__restrict__ z, int ncols,
@@ -283,6 +391,33 @@ hipError_t launch_silu_mul_q8_1(const float *g, const float *u, float *h, int8_t
                                 int ncols, int nrows, hipStream_t s) {
   const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
   hipLaunchKernelGGL(k_silu_mul_q8_1, grid, dim3(kThreads), 0, s, g, u, h, qs, d, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_gated_rms_norm(const float *o, const float *g, const float *w, float *z,
+                                 int ncols, int head_dim, int nrows, float eps, hipStream_t s) {
+  const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
+  switch (head_dim) {
+    case 32: hipLaunchKernelGGL(k_gated_rms_norm<32>, grid, dim3(kThreads), 0, s, o, g, w, z, ncols, eps); break;
+    case 64: hipLaunchKernelGGL(k_gated_rms_norm<64>, grid, dim3(kThreads), 0, s, o, g, w, z, ncols, eps); break;
+    case 128: hipLaunchKernelGGL(k_gated_rms_norm<128>, grid, dim3(kThreads), 0, s, o, g, w, z, ncols, eps); break;
+    case 256: hipLaunchKernelGGL(k_gated_rms_norm<256>, grid, dim3(kThreads), 0, s, o, g, w, z, ncols, eps); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gated_rmsnorm_q8_1(const float *o, const float *g, const float *w, float *z,
+                                     int8_t *qs, float *d, int ncols, int head_dim, int nrows,
+                                     float eps, hipStream_t s) {
+  const dim3 grid((ncols + kColsPerPass - 1) / kColsPerPass, nrows);
+  switch (head_dim) {
+    case 32: hipLaunchKernelGGL(k_gated_rmsnorm_q8_1<32>, grid, dim3(kThreads), 0, s, o, g, w, z, qs, d, ncols, eps); break;
+    case 64: hipLaunchKernelGGL(k_gated_rmsnorm_q8_1<64>, grid, dim3(kThreads), 0, s, o, g, w, z, qs, d, ncols, eps); break;
+    case 128: hipLaunchKernelGGL(k_gated_rmsnorm_q8_1<128>, grid, dim3(kThreads), 0, s, o, g, w, z, qs, d, ncols, eps); break;
+    case 256: hipLaunchKernelGGL(k_gated_rmsnorm_q8_1<256>, grid, dim3(kThreads), 0, s, o, g, w, z, qs, d, ncols, eps); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -115,6 +115,35 @@ int silu_mul_q8_1(const float *gate, const float *up, float *h, int8_t *qs, floa
                   int nrows, void *stream);
 
 /*
+ * gated_rms_norm_f32 -- first half of the KDA gated-norm producer chain.
+ * Source: q8_fuse_gate.rs, module doc and `main` (the KDA qkv width, 64 heads x 128 head_dim
+ * = 8192, is the KDA gated-norm site, still on the unfused chain).  The page gives no formula;
+ * the rule is the output stage of a Kimi-delta-attention layer: RMSNorm over each head's
+ * head_dim values, a gain shared by the heads, then the sigmoid output gate.  For each row r
+ * and head h (columns h*head_dim .. h*head_dim + head_dim - 1), every step in f64 and one
+ * rounding to f32 at the end:
+ *   s = 1 / sqrt(sum_{j in h} o[r, j]^2 / head_dim + eps)
+ *   z[r, j] = (float)(((o[r, j] * w[j mod head_dim]) * s) * (1 / (1 + exp(-g[r, j]))))
+ *   o, g, z   f32 [nrows, ncols], 16-byte aligned; z may not alias o or g
+ *   w         f32 [head_dim], 16-byte aligned
+ *   head_dim  32, 64, 128 or 256;  ncols a multiple of 32 and of head_dim, <= FP8GEMV_MAX_IN_F;
+ *             1 <= nrows <= FP8GEMV_MAX_M;  eps as for rms_norm_f32 (1e-6 on the page)
+ * The chain is gated_rms_norm_f32 then quantize_q8_1.
+ */
+int gated_rms_norm_f32(const float *o, const float *g, const float *w, float *z, int ncols,
+                       int head_dim, int nrows, float eps, void *stream);
+
+/*
+ * gated_rmsnorm_q8_1 -- the fused KDA gated-norm producer: gated_rms_norm_f32 then
+ * quantize_q8_1 in one launch, byte-identical in z, qs and d to that chain.  z may be NULL
+ * (not stored).  Source: as above, with the fused-producer contract of q8_fuse_gate.rs's
+ * module doc.
+ *   qs int8 [nrows, ncols] (16-byte aligned), d f32 [nrows, ncols / 32] (4-byte aligned)
+ */
+int gated_rmsnorm_q8_1(const float *o, const float *g, const float *w, float *z, int8_t *qs,
+                       float *d, int ncols, int head_dim, int nrows, float eps, void *stream);
+
+/*
  * gemv_q8_0_q81 -- matvec over ggml Q8_0 weight rows.
  * Source: gemv_e4m3_bench.rs, QUESTION and THE COMPARISON (arm Q8_0: 34 bytes per 32
  * weights, an fp16 scale then 32 int8, row_bytes = in_f / 32 * 34) and `synth_q8_0`.

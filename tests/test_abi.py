@@ -31,6 +31,7 @@ def fg():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1",
                                   "silu_mul_f32", "silu_mul_q8_1",
+                                  "gated_rms_norm_f32", "gated_rmsnorm_q8_1",
                                   "gemv_q8_0_q81", "gemv_e4m3_q81", "gemv_e4m3_blk128_q81",
                                   "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
                                   "fp8gemv_read_bytes", "fp8gemv_read_pattern",
@@ -151,6 +152,29 @@ def test_requant_argument_errors(fg):
     assert L.requant_e4m3_q8_0(FAKE, 64, 1.0, FAKE, 69, 64, 8, None) == e.FP8GEMV_ERR_ALIGN
     assert L.requant_e4m3_blk128_q8_0(FAKE, 64, FAKE + 2, 1, FAKE, 68, 64, 8,
                                       None) == e.FP8GEMV_ERR_ALIGN
+
+
+def test_gated_producer_argument_errors(fg):
+    L = fg.lib()
+    e = fg
+    F = FAKE
+    assert L.gated_rms_norm_f32(None, F, F, F, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_NULL
+    assert L.gated_rms_norm_f32(F, F, F, None, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_NULL
+    assert L.gated_rmsnorm_q8_1(F, F, None, None, F, F, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_NULL
+    assert L.gated_rmsnorm_q8_1(F, F, F, None, None, F, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_NULL
+    for ncols, hd, nrows in ((8192, 96, 1), (8192, 512, 1), (8160, 128, 1), (8192, 128, 0),
+                             (8200, 32, 1), (0, 32, 1)):
+        assert L.gated_rmsnorm_q8_1(F, F, F, None, F, F, ncols, hd, nrows, 1e-6,
+                                    None) == e.FP8GEMV_ERR_SHAPE, (ncols, hd, nrows)
+    assert L.gated_rmsnorm_q8_1(F, F, F, None, F, F, 65536 + 256, 256, 1, 1e-6,
+                                None) == e.FP8GEMV_ERR_TOO_LARGE
+    assert L.gated_rmsnorm_q8_1(F, F, F, None, F, F, 8192, 128, 65536, 1e-6,
+                                None) == e.FP8GEMV_ERR_TOO_LARGE
+    assert L.gated_rmsnorm_q8_1(F + 4, F, F, None, F, F, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gated_rmsnorm_q8_1(F, F, F + 8, None, F, F, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gated_rmsnorm_q8_1(F, F, F, F + 4, F, F, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gated_rmsnorm_q8_1(F, F, F, None, F, F + 2, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_ALIGN
+    assert L.gated_rms_norm_f32(F, F, F, F + 8, 8192, 128, 1, 1e-6, None) == e.FP8GEMV_ERR_ALIGN
 
 
 def test_read_bytes_argument_errors(fg):
