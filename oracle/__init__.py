@@ -143,6 +143,14 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float = EPS):
     return z64, z64.astype(np.float32), s64
 
 
+def _exp(t: float) -> float:
+    """libm exp with IEEE overflow to +inf (Python's math.exp raises instead)."""
+    try:
+        return math.exp(t)
+    except OverflowError:
+        return math.inf
+
+
 def gated_rms_norm(o: np.ndarray, g: np.ndarray, w: np.ndarray, head_dim: int,
                    eps: float = EPS):
     """KDA gated-norm of f32 rows o [nrows, ncols] with output gate g [nrows, ncols] and gain
@@ -171,7 +179,7 @@ def gated_rms_norm(o: np.ndarray, g: np.ndarray, w: np.ndarray, head_dim: int,
             sl = slice(h * head_dim, (h + 1) * head_dim)
             ss = math.fsum(o64[r, sl] * o64[r, sl])
             s = 1.0 / math.sqrt(ss / head_dim + eps64)
-            gate = np.array([1.0 / (1.0 + math.exp(-v)) for v in g64[r, sl]])
+            gate = np.array([1.0 / (1.0 + _exp(-v)) for v in g64[r, sl]])
             z64[r, sl] = ((o64[r, sl] * w64) * s) * gate
     return z64, z64.astype(np.float32)
 
