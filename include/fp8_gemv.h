@@ -21,6 +21,8 @@
  *   - Sizes are elements unless named *_bytes.  Matrices are row-major.
  *   - q8_1 activation = two planes: qs int8 [rows, cols] and d f32 [rows, cols/32] (one
  *     scale per 32 consecutive values, d = amax/127; value = d * qs).  No per-block sum.
+ *     A block whose amax is nonzero but below 127 * 2^-128 (about 3.7e-37) has no finite
+ *     1 / d in f32; its qs are unspecified (documented, not checked).
  *   - Preconditions that are documented but not checked: no NaN/Inf in x, w, scales or grid;
  *     no e4m3 NaN code (0x7F, 0xFF) in a weight plane (the bench page's generator excludes
  *     it and says the real dispatch refuses it); buffers large enough for the sizes passed.

@@ -200,7 +200,8 @@ def quantize_q8_1(z: np.ndarray):
     d = np.empty((nrows, ncols // 32), dtype=np.float32)
     rc = _load().oracle_quantize_q8_1(z.ctypes.data, nrows, ncols, qs.ctypes.data, d.ctypes.data)
     if rc != 0:
-        raise ValueError(f"oracle_quantize_q8_1: bad shape ({rc})")
+        raise ValueError(f"oracle_quantize_q8_1 refused its input ({rc}): "
+                         + ("a block with no finite 1/d" if rc == -1 else "bad shape"))
     return qs, d
 
 

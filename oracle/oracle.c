@@ -62,7 +62,9 @@ double oracle_fp16_value(uint16_t bits) {
  *   d    = amax / 127
  *   id   = 1 / d   (0 when d == 0)
  *   q_i  = round(z_i * id), halves away from zero (C roundf)
- * Returns 0, or -2 when ncols is not a multiple of 32. */
+ * Returns 0, -1 for a refused input (a block whose amax is nonzero but so small, below
+ * 127 * 2^-128, that 1 / d overflows f32: the rule gives no integer there), or -2 when ncols
+ * is not a multiple of 32. */
 int oracle_quantize_q8_1(const float *z, int nrows, int ncols, int8_t *qs, float *d) {
     if (ncols % 32 != 0 || nrows < 0 || ncols < 0) return -2;
     int nb = ncols / 32;
@@ -76,6 +78,7 @@ int oracle_quantize_q8_1(const float *z, int nrows, int ncols, int8_t *qs, float
             }
             float db = amax / 127.0f;
             float id = (db != 0.0f) ? 1.0f / db : 0.0f;
+            if (!isfinite(id)) return -1;
             for (int i = 0; i < 32; ++i) {
                 float v = zb[i] * id;
                 qs[(int64_t)r * ncols + 32 * b + i] = (int8_t)roundf(v);

@@ -81,12 +81,14 @@ def test_gated_rmsnorm_q8_1_matches_oracle_and_chain(fg, ncols, head_dim, nrows)
 
 
 def test_gated_special_values(fg):
-    # saturated gates (+-100, +-1e30), a zero gate, a zero head (d = 0 blocks) and tiny heads
+    # saturated gates (100, +-1e30), a nearly closed gate (-30: z ~ 1e-13 stays a normal f32,
+    # so every block has a finite 1/d), a zero gate, a zero head (d = 0 blocks) and a head of
+    # tiny values
     case("gated_rmsnorm_q8_1 special values")
     head_dim, ncols = 128, 1024
     o, g, w = _inputs(ncols, head_dim, 1)
     g[0, :128] = 100.0
-    g[0, 128:256] = -100.0
+    g[0, 128:256] = -30.0
     g[0, 256:384] = 0.0
     g[0, 384:512:2] = 1e30
     g[0, 385:512:2] = -1e30
