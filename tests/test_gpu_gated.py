@@ -103,9 +103,11 @@ def test_gated_special_values(fg):
 
 
 def test_gated_rejects_bad_head_dim(fg):
-    o = torch.zeros(256, device=dev())
-    qs = torch.zeros(256, dtype=torch.int8, device=dev())
-    d = torch.zeros(8, device=dev())
+    # buffers large enough for every size tried, so that the library (not the binding's size
+    # check) is what refuses the head_dim
+    o = torch.zeros(1024, device=dev())
+    qs = torch.zeros(1024, dtype=torch.int8, device=dev())
+    d = torch.zeros(32, device=dev())
     for hd, ncols in ((48, 192), (512, 512), (128, 192)):
         with pytest.raises(fg.Fp8GemvError):
             fg.gated_rmsnorm_q8_1(o, o, o, None, qs, d, ncols, hd, 1)
