@@ -89,8 +89,12 @@ def _assert_close(y, yo, A, rows=None):
 # rows of an odd number of windows (Q8_0: 12 and 32 groups of 8 blocks, in windows of three
 # groups, the last one partial), 8224 leaves a 32-column last e4m3 window, 9600 is not a
 # multiple of 256 (Q8_0 generic path), 24576 is the largest in_f of that launch shape.
+# More Q8_0 row lengths (in groups of 8 blocks): 9, 10, 12, 48 and 95 groups (last windows of
+# 0, 1 or 2 groups past whole windows of three), single rows at the bench's in_f values, and
+# out_f values that leave the last workgroup partly empty.
 SMALL = [(1, 32), (7, 96), (130, 160), (131, 288), (257, 1056), (300, 2080), (64, 4096),
-         (129, 4352), (33, 1280), (250, 2048), (37, 8704), (5, 8224), (131, 9600), (9, 24576)]
+         (129, 4352), (33, 1280), (250, 2048), (37, 8704), (5, 8224), (131, 9600), (9, 24576),
+         (13, 2304), (21, 2560), (43, 3072), (7, 12288), (11, 24320), (1, 5120), (3, 17408)]
 
 
 @pytest.mark.parametrize("m", [1, 3, 5])
