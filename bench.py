@@ -35,6 +35,8 @@ METRIC = "µs/GEMV and weight-stream HBM GB/s (% of peak) at m=1, 27B-class shap
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 LLC_BYTES = 256 * 1024 * 1024  # MI355X last-level (Infinity) cache
 SHAPES = [(5120, 5120), (17408, 5120), (5120, 17408)]  # [out_f, in_f]
+# read patterns that stream whole Q8_0 rows (timed over Q8_0-sized planes)
+Q8_PATTERNS = ("rows_816", "rows_aligned", "line_windows")
 ARMS = ["e4m3", "blk128", "q8_0"]
 SCALE = 2.0 ** -4
 EPS = 1e-6
@@ -751,7 +753,7 @@ def main() -> int:
     # Q8_0 planes of the same shapes and their multiples), cold by rotation, each fitted as
     # t = fixed + bytes / steady.  The best pattern at each size is the ceiling the GEMVs are
     # compared with.
-    ceiling, read_patterns, read_fit = {}, {}, None
+    ceiling, q8_ceiling, read_patterns, read_fit = {}, {}, {}, None
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     if not (args.kernels_only or args.no_read_patterns):
         e4_small, e4 = weight_bytes("e4m3", 5120, 5120), weight_bytes("e4m3", 17408, 5120)
@@ -766,7 +768,9 @@ def main() -> int:
         for pat, rb, sizes in (("chunk8k", 0, None), ("chunk16k", 0, None), ("wg8", 0, None),
                                ("wg16", 0, None), ("persistent", 0, None), ("cached", 0, None),
                                ("rows_1k", 5120, None),
-                               ("rows_816", 5440, (q8_small, q8, 2 * q8, 4 * q8))):
+                               ("rows_816", 5440, (q8_small, q8, 2 * q8, 4 * q8)),
+                               ("rows_aligned", 5440, (q8_small, q8, 2 * q8, 4 * q8)),
+                               ("line_windows", 5440, (q8_small, q8, 2 * q8, 4 * q8))):
             pts = []
             for nbytes in sizes or (e4_small, e4, 2 * e4, 4 * e4):
                 bufs = pool(nbytes)
@@ -781,12 +785,18 @@ def main() -> int:
         del pools
         torch.cuda.empty_cache()
         for shape, nbytes in (("5120x5120", e4_small), ("17408x5120", e4), ("5120x17408", e4)):
-            best = min(((p, pt["us"]) for p, f in read_patterns.items() if p != "rows_816"
+            best = min(((p, pt["us"]) for p, f in read_patterns.items() if p not in Q8_PATTERNS
                         for pt in f["points"] if pt["bytes"] == nbytes), key=lambda x: x[1])
             ceiling[shape] = {"bytes": nbytes, "us": best[1], "pattern": best[0],
                               "GBs": round(nbytes / best[1] / 1e3, 1),
                               "pct_peak": round(100 * nbytes / best[1] / 1e3 / HBM_PEAK_GBS, 1)}
-        best_pat = min((p for p in read_patterns if p != "rows_816"),
+        # the same over the Q8_0 planes, from the patterns that read whole Q8_0 rows
+        for shape, nbytes in (("5120x5120", q8_small), ("17408x5120", q8)):
+            best = min(((p, pt["us"]) for p in Q8_PATTERNS for pt in read_patterns[p]["points"]
+                        if pt["bytes"] == nbytes), key=lambda x: x[1])
+            q8_ceiling[shape] = {"bytes": nbytes, "us": best[1], "pattern": best[0],
+                                 "GBs": round(nbytes / best[1] / 1e3, 1)}
+        best_pat = min((p for p in read_patterns if p not in Q8_PATTERNS),
                        key=lambda p: next(pt["us"] for pt in read_patterns[p]["points"]
                                           if pt["bytes"] == e4))
         read_fit = dict(read_patterns[best_pat], pattern=best_pat)
@@ -796,6 +806,8 @@ def main() -> int:
         shape = k.split("@")[1]
         if shape in ceiling:
             v["pct_of_read_ceiling"] = round(100 * (v["weight_GBs"] / ceiling[shape]["GBs"]), 1)
+        if k.startswith("q8_0@") and shape in q8_ceiling:
+            v["pct_of_q8_0_read_ceiling"] = round(100 * (v["weight_GBs"] / q8_ceiling[shape]["GBs"]), 1)
 
     # Producer alone (latency-bound; the gate page's site widths), fused vs two-launch chain.
     prod_us = {}
@@ -976,7 +988,8 @@ def main() -> int:
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
         "gemv": detail, "read_ceiling": ceiling, "read_fit": read_fit,
-        "read_patterns": read_patterns, "fixed_cost": fixed, "m_rows": m_rows, "sheets": sheets,
+        "read_patterns": read_patterns, "q8_0_read_ceiling": q8_ceiling, "fixed_cost": fixed,
+        "m_rows": m_rows, "sheets": sheets,
         "requant": requant,
         "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu, "cold_check": cold,

@@ -333,12 +333,16 @@ FP8GEMV_READ_ROWS_1K = 6
 FP8GEMV_READ_ROWS_816 = 7
 FP8GEMV_READ_EMPTY = 8
 FP8GEMV_READ_ONE_WAVE = 9
-FP8GEMV_READ_NUM_PATTERNS = 10
+FP8GEMV_READ_ROWS_ALIGNED = 10
+FP8GEMV_READ_LINE_WINDOWS = 11
+FP8GEMV_READ_NUM_PATTERNS = 12
 READ_PATTERNS = {"chunk8k": FP8GEMV_READ_CHUNK8K, "chunk16k": FP8GEMV_READ_CHUNK16K,
                  "wg8": FP8GEMV_READ_WG8, "wg16": FP8GEMV_READ_WG16,
                  "persistent": FP8GEMV_READ_PERSISTENT, "cached": FP8GEMV_READ_CACHED,
                  "rows_1k": FP8GEMV_READ_ROWS_1K, "rows_816": FP8GEMV_READ_ROWS_816,
-                 "empty": FP8GEMV_READ_EMPTY, "one_wave": FP8GEMV_READ_ONE_WAVE}
+                 "empty": FP8GEMV_READ_EMPTY, "one_wave": FP8GEMV_READ_ONE_WAVE,
+                 "rows_aligned": FP8GEMV_READ_ROWS_ALIGNED,
+                 "line_windows": FP8GEMV_READ_LINE_WINDOWS}
 
 
 def fp8gemv_read_pattern(buf, nbytes: int, pattern: str, sink, row_bytes: int = 0,

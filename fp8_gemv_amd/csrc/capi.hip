@@ -185,7 +185,8 @@ int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_
                          uint32_t *sink, void *stream) {
   if (!p || !sink) return FP8GEMV_ERR_NULL;
   if (bytes < 1 || pattern < 0 || pattern >= FP8GEMV_READ_NUM_PATTERNS) return FP8GEMV_ERR_SHAPE;
-  if (pattern == FP8GEMV_READ_ROWS_1K || pattern == FP8GEMV_READ_ROWS_816) {
+  if (pattern == FP8GEMV_READ_ROWS_1K || pattern == FP8GEMV_READ_ROWS_816 ||
+      pattern == FP8GEMV_READ_ROWS_ALIGNED || pattern == FP8GEMV_READ_LINE_WINDOWS) {
     if (row_bytes < 1024 || row_bytes > (1 << 20) || row_bytes % 16 != 0 || bytes % row_bytes != 0)
       return FP8GEMV_ERR_SHAPE;
   }

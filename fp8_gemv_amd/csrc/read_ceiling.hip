@@ -117,6 +117,81 @@ void k_read_rows(const uint8_t *__restrict__ p, int64_t row_bytes, int64_t rows,
   keep(x, sink);
 }
 
+// Rows of row_bytes, one wave per row, each row read from the 128-byte line boundary at or
+// before its first byte in 1 KiB windows (every wave-wide load covers 8 whole lines); the
+// bytes before the row lie before its resource (negative offsets, wrapped) and read as zeros.
+// Batches of 3 windows with the next batch in flight.
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_read_rows_aligned(const uint8_t *__restrict__ p, int64_t row_bytes, int64_t rows,
+                         uint32_t *__restrict__ sink) {
+  constexpr int U = 3;
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  const bool ok = row < rows;
+  const uint8_t *rp = p + (ok ? row * row_bytes : 0);
+  const rsrc_t rs = buf_rsrc(rp, ok ? (uint32_t)row_bytes : 0u);
+  const uint32_t pre = (uint32_t)(reinterpret_cast<uintptr_t>(rp) & 127u);
+  const uint32_t lo = (uint32_t)lane * 16 - pre;  // wraps for the lanes before the row
+  const int nwin = (int)((pre + (uint64_t)row_bytes + 1023) / 1024);
+  int4_t a[U], b[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) a[u] = load16<kAuxNonTemporal>(rs, lo + u * 1024);
+  uint32_t x = 0;
+  for (int w0 = 0; w0 < nwin; w0 += 2 * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) b[u] = load16<kAuxNonTemporal>(rs, lo + (w0 + U + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= fold(a[u]);
+    if (w0 + U >= nwin) break;
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = load16<kAuxNonTemporal>(rs, lo + (w0 + 2 * U + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= fold(b[u]);
+  }
+  keep(x, sink);
+}
+
+// Line windows: a 4-wave workgroup owns R consecutive rows (R * row_bytes a multiple of 2176
+// when there are R of them) and reads them as one span of 2176-byte windows (17 whole lines;
+// for Q8_0 rows, 8 groups of 8 blocks), window K by wave K % 4, each as lines 0-7 and 8-15 (64
+// lanes) and line 16 (8 lanes).  Batches of 2 windows with the next batch in flight.
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_read_line_windows(const uint8_t *__restrict__ p, int64_t row_bytes, int64_t rows, int R,
+                         uint32_t *__restrict__ sink) {
+  constexpr int U = 2;
+  constexpr uint32_t kWin = 2176;
+  const int lane = threadIdx.x % kWave, w = wave_id();
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int64_t nr = r0 < rows ? (rows - r0 < R ? rows - r0 : R) : 0;
+  const uint32_t span = (uint32_t)(nr * row_bytes);
+  const rsrc_t rs = buf_rsrc(p + (nr ? r0 * row_bytes : 0), span);
+  const int nwin = (int)((span + kWin - 1) / kWin);
+  const int nmine = nwin > w ? (nwin - w + 3) / 4 : 0;
+  auto base = [&](int i) -> uint32_t { return i < nmine ? (uint32_t)(w + 4 * i) * kWin : 0x40000000u; };
+  const uint32_t lo = (uint32_t)lane * 16, lc = lane < 8 ? 2048u + (uint32_t)lane * 16 : 0x40000000u;
+  int4_t a[U][3], b[U][3];
+  auto load3 = [&](int4_t (&v)[3], uint32_t bb) {
+    v[0] = load16<kAuxNonTemporal>(rs, bb + lo);
+    v[1] = load16<kAuxNonTemporal>(rs, bb + 1024 + lo);
+    v[2] = load16<kAuxNonTemporal>(rs, bb + lc);
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) load3(a[u], base(u));
+  uint32_t x = 0;
+  for (int w0 = 0; w0 < nmine; w0 += 2 * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load3(b[u], base(w0 + U + u));
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= fold(a[u][0]) ^ fold(a[u][1]) ^ fold(a[u][2]);
+    if (w0 + U >= nmine) break;
+#pragma unroll
+    for (int u = 0; u < U; ++u) load3(a[u], base(w0 + 2 * U + u));
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= fold(b[u][0]) ^ fold(b[u][1]) ^ fold(b[u][2]);
+  }
+  keep(x, sink);
+}
+
 // The grid of the 8 KiB-per-wave pattern with no loads: what dispatch and drain cost alone.
 __global__ __launch_bounds__(4 * kWave) void k_read_empty(int64_t bytes, uint32_t *__restrict__ sink) {
   if (bytes < 0 && threadIdx.x == 0) sink[0] = 0;  // never: bytes >= 1
@@ -173,6 +248,19 @@ hipError_t launch_read_pattern(const void *pv, int64_t bytes, int pattern, int64
       if (pattern == FP8GEMV_READ_ROWS_1K)
         return launch(k_read_rows<64>, grid, 4 * kWave, s, p, row_bytes, rows, sink);
       return launch(k_read_rows<51>, grid, 4 * kWave, s, p, row_bytes, rows, sink);
+    }
+    case FP8GEMV_READ_ROWS_ALIGNED: {
+      const int64_t rows = bytes / row_bytes;
+      return launch(k_read_rows_aligned, (unsigned)((rows + 3) / 4), 4 * kWave, s, p, row_bytes,
+                    rows, sink);
+    }
+    case FP8GEMV_READ_LINE_WINDOWS: {
+      const int64_t rows = bytes / row_bytes;
+      int64_t g = 2176, r = row_bytes;
+      while (r) { const int64_t t = g % r; g = r; r = t; }  // gcd(2176, row_bytes)
+      const int R = (int)(2176 / g);
+      return launch(k_read_line_windows, (unsigned)((rows + R - 1) / R), 4 * kWave, s, p,
+                    row_bytes, rows, R, sink);
     }
     case FP8GEMV_READ_EMPTY:
       return launch(k_read_empty, (unsigned)((bytes + 32767) / 32768), 4 * kWave, s, bytes, sink);

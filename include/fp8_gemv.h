@@ -259,12 +259,19 @@ int fp8gemv_read_bytes(const void *p, int64_t bytes, uint32_t *sink, void *strea
  *                            of 4 with the next batch in flight (the e4m3 GEMV's m = 1 pattern)
  *   FP8GEMV_READ_ROWS_816    the same with 816-byte windows read by 51 lanes (the Q8_0 GEMV's
  *                            pattern: three 272-byte groups of eight 34-byte blocks)
+ *   FP8GEMV_READ_ROWS_ALIGNED  rows of row_bytes, one wave per row, each row read from the
+ *                            128-byte line boundary at or before its start in 1 KiB windows
+ *                            (whole lines per wave-wide load), batches of 3
+ *   FP8GEMV_READ_LINE_WINDOWS  4-wave workgroups each read R consecutive rows (the smallest R
+ *                            with R * row_bytes a multiple of 2176) as one span of 2176-byte
+ *                            windows (17 whole lines; 8 groups of Q8_0 blocks), window K by
+ *                            wave K % 4 as two 1 KiB loads and one 128-byte line, batches of 2
  *   FP8GEMV_READ_EMPTY       CHUNK8K's grid with no loads: dispatch and drain alone
  *   FP8GEMV_READ_ONE_WAVE    one wave loads the first min(bytes, 1 KiB): a launch plus one cold
  *                            round trip to HBM
  *   p, bytes, sink   as for fp8gemv_read_bytes
- *   row_bytes        ROWS_* patterns only: 1024 <= row_bytes <= 2^20, a multiple of 16, and
- *                    bytes a multiple of it; ignored by the other patterns
+ *   row_bytes        ROWS_* and LINE_WINDOWS only: 1024 <= row_bytes <= 2^20, a multiple of
+ *                    16, and bytes a multiple of it; ignored by the other patterns
  * Returns FP8GEMV_ERR_SHAPE for an unknown pattern or a bad row_bytes.
  */
 #define FP8GEMV_READ_CHUNK8K     0
@@ -277,7 +284,9 @@ int fp8gemv_read_bytes(const void *p, int64_t bytes, uint32_t *sink, void *strea
 #define FP8GEMV_READ_ROWS_816    7
 #define FP8GEMV_READ_EMPTY       8
 #define FP8GEMV_READ_ONE_WAVE    9
-#define FP8GEMV_READ_NUM_PATTERNS 10
+#define FP8GEMV_READ_ROWS_ALIGNED 10
+#define FP8GEMV_READ_LINE_WINDOWS 11
+#define FP8GEMV_READ_NUM_PATTERNS 12
 int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_bytes,
                          uint32_t *sink, void *stream);
 

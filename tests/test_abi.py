@@ -219,7 +219,7 @@ def test_read_pattern_argument_errors(fg):
     assert L.fp8gemv_read_pattern(FAKE, 0, 0, 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
     assert L.fp8gemv_read_pattern(FAKE, 1024, -1, 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
     assert L.fp8gemv_read_pattern(FAKE, 1024, len(P), 0, FAKE, None) == fg.FP8GEMV_ERR_SHAPE
-    for rows in ("rows_1k", "rows_816"):
+    for rows in ("rows_1k", "rows_816", "rows_aligned", "line_windows"):
         for rb, nbytes in ((0, 4096), (1008, 4032), (1040, 4096), (1024 + 8, 2064),
                            ((1 << 20) + 16, (1 << 20) + 16)):
             assert L.fp8gemv_read_pattern(FAKE, nbytes, P[rows], rb, FAKE,

@@ -357,7 +357,8 @@ def test_read_bytes_measurement_kernel_runs(fg):
 
 
 @pytest.mark.parametrize("pattern", ["chunk8k", "chunk16k", "wg8", "wg16", "persistent",
-                                     "cached", "rows_1k", "rows_816", "empty", "one_wave"])
+                                     "cached", "rows_1k", "rows_816", "empty", "one_wave",
+                                     "rows_aligned", "line_windows"])
 def test_read_patterns_run(fg, pattern):
     # Every measurement pattern over ragged and whole ranges; the rows patterns over rows of
     # 5120 and 5440 bytes (the e4m3 and Q8_0 rows at in_f = 5120).  Nothing is computed, so
@@ -365,7 +366,7 @@ def test_read_patterns_run(fg, pattern):
     case(f"fp8gemv_read_pattern {pattern}")
     buf = torch.randint(0, 255, (64 * 5440,), dtype=torch.uint8, device=dev())
     sink = torch.full((1,), 7, dtype=torch.int32, device=dev())
-    if pattern.startswith("rows"):
+    if pattern.startswith("rows") or pattern == "line_windows":
         for rb in (5120, 5440):
             for rows in (1, 5, 64):
                 fg.fp8gemv_read_pattern(buf, rows * rb, pattern, sink, row_bytes=rb)
