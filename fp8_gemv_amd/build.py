@@ -22,6 +22,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 SOURCES = {
     "producer.hip": ["-ffp-contract=off"],
     "gemv_e4m3.hip": [],
+    "gemv_e4m3_mfma.hip": [],
     "gemv_q8_0.hip": [],
     "read_ceiling.hip": [],
     "requant.hip": ["-ffp-contract=off"],

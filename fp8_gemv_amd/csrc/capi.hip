@@ -209,7 +209,7 @@ int fp8gemv_gemv_launch_info(int container, const void *W, int64_t row_bytes, in
   } else if (container == FP8GEMV_E4M3 || container == FP8GEMV_E4M3_BLK128) {
     if (row_bytes < in_f) return FP8GEMV_ERR_ROW_BYTES;
     if (!aligned(W, 16) || row_bytes % 16 != 0) return FP8GEMV_ERR_ALIGN;
-    r = fp8gemv::describe_gemv_e4m3(container == FP8GEMV_E4M3_BLK128, m, in_f, out_f);
+    r = fp8gemv::describe_gemv_e4m3(container == FP8GEMV_E4M3_BLK128, row_bytes, m, in_f, out_f);
   } else {
     return FP8GEMV_ERR_SHAPE;
   }

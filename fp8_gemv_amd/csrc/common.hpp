@@ -149,7 +149,15 @@ hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, co
                             float *y, int m, int in_f, int out_f, hipStream_t s);
 hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
                             const float *d, float *y, int m, int in_f, int out_f, hipStream_t s);
-LaunchDesc describe_gemv_e4m3(bool blk128, int m, int in_f, int out_f);
+LaunchDesc describe_gemv_e4m3(bool blk128, int64_t row_bytes, int m, int in_f, int out_f);
+// The matrix-core kernel for several activation rows (gemv_e4m3_mfma.hip); launch_gemv_e4m3
+// and describe_gemv_e4m3 choose it where gemv_e4m3_mfma_applies.
+bool gemv_e4m3_mfma_applies(int64_t row_bytes, int m, int in_f);
+hipError_t launch_gemv_e4m3_mfma(const uint8_t *W, int64_t row_bytes, float scale,
+                                 const float *grid, int grid_cols, bool blk128, const int8_t *qs,
+                                 const float *d, float *y, int m, int in_f, int out_f,
+                                 hipStream_t s);
+LaunchDesc describe_gemv_e4m3_mfma(bool blk128, int m, int in_f, int out_f);
 LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f);
 hipError_t launch_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                                int grid_cols, bool blk128, void *Wq, int64_t q_row_bytes,

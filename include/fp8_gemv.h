@@ -172,6 +172,11 @@ int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const floa
  *   row_bytes  >= in_f, multiple of 16;  W 16-byte aligned
  *   scale      per-tensor dequantisation factor, applied once per output
  *   qs, d, y   as for gemv_q8_0_q81
+ * Each activation row is computed independently.  For m <= 4, or in_f > 8192, row t of an
+ * m-row call is bit-identical to an m=1 call on that row.  For 5 <= m and in_f <= 8192 the
+ * products run on the matrix cores with a different (fixed) summation order: row t is then
+ * bit-identical to the same row in any other call with m >= 5, whatever its position and the
+ * other rows, and agrees with m=1 to rounding.
  */
 int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
                   const float *d, float *y, int m, int in_f, int out_f, void *stream);
@@ -184,7 +189,8 @@ int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t
  * y[t, r] = sum_k grid[r/128, k/128] * e4m3(W[r, k]) * d_a[t, k/32] * qs[t, k]
  *   grid       f32 [ceil(out_f/128), grid_cols], row-major, a multiplier
  *   grid_cols  must equal ceil(in_f / 128)
- *   other arguments as for gemv_e4m3_q81
+ *   other arguments, and the summation order for several activation rows, as for
+ *   gemv_e4m3_q81
  */
 int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid, int grid_cols,
                          const int8_t *qs, const float *d, float *y, int m, int in_f, int out_f,

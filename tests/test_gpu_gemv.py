@@ -141,20 +141,81 @@ def test_gemv_sheet_shapes_every_row(fg, kind, out_f, in_f):
     _assert_close(y, yo, A)
 
 
+def on_matrix_cores(kind, m, in_f):
+    """The e4m3 containers take the matrix-core kernel for m >= 5 up to in_f = 8192."""
+    return kind != "q8_0" and m >= 5 and in_f <= 8192
+
+
+def row_reference(fg, c, t, m):
+    """Row t of activation rows qs/d computed alone: an m = 1 call, or, where an m-row call
+    runs on the matrix cores, a 5-row call holding row t first and four other rows after it."""
+    if not on_matrix_cores(c.kind, m, c.in_f):
+        return c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)[0]
+    idx = [t] + [(t + k) % c.m for k in range(1, 5)]
+    return c.gpu(fg, qs=to_dev(c.qs[idx]), d=to_dev(c.d[idx]), m=5)[0]
+
+
 # m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
-# m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.
+# m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.  Each row
+# of an m-row call is bit-identical to the same row computed alone: to an m = 1 call on the
+# vector path, and on the matrix cores (e4m3 containers, m >= 5, in_f <= 8192) to that row at
+# another position among other rows.
 @pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("kind", KINDS)
-def test_gemv_m_rows_bit_identical_to_m1(fg, kind, out_f, in_f):
+def test_gemv_m_rows_bit_identical_per_row(fg, kind, out_f, in_f):
     c = Case(kind, out_f, in_f, 11)
     for m in (1, 2, 3, 4, 5, 8, 11):
         case(f"{kind} m={m} out_f={out_f} in_f={in_f}")
         y = c.gpu(fg, qs=to_dev(c.qs[:m]), d=to_dev(c.d[:m]), m=m)
         for t in range(m):
-            y1 = c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)
-            assert y[t].tobytes() == y1[0].tobytes(), (m, t)
+            y1 = row_reference(fg, c, t, m)
+            assert y[t].tobytes() == y1.tobytes(), (m, t)
     # the last call (m = 11, two weight passes) against the oracle at every output
     yo, A = c.oracle_all()
+    _assert_close(y, yo, A)
+
+
+# The matrix-core kernel at its edges: in_f not a multiple of its 256-column step or of the
+# 1 KiB group of 4 steps, in_f = 8192 (its largest) and 8224 (the vector path again), out_f
+# not a multiple of a wave's 16 rows or a workgroup's 64, block-128 grids with several row
+# tiles, m = 8 (one full pass), 9 and 17 (a last pass of one row), 16 (two full passes).
+MFMA_SHAPES = [(1, 32), (17, 288), (100, 1056), (200, 4128), (129, 8160), (65, 8192),
+               (33, 8224), (300, 5120)]
+
+
+@pytest.mark.parametrize("m", [5, 8, 9, 16, 17])
+@pytest.mark.parametrize("out_f,in_f", MFMA_SHAPES)
+@pytest.mark.parametrize("kind", ["e4m3", "blk128"])
+def test_gemv_matrix_core_shapes_match_oracle(fg, kind, out_f, in_f, m):
+    case(f"{kind} matrix cores out_f={out_f} in_f={in_f} m={m}")
+    c = Case(kind, out_f, in_f, m)
+    y = c.gpu(fg)
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+
+
+@pytest.mark.parametrize("kind", ["e4m3", "blk128"])
+def test_gemv_matrix_core_rows_independent_of_order(fg, kind):
+    # the same 8 rows in reverse order give each row the same bits
+    case(f"{kind} matrix cores, rows reversed")
+    c = Case(kind, 300, 5120, 8)
+    y = c.gpu(fg)
+    rev = list(range(7, -1, -1))
+    yr = c.gpu(fg, qs=to_dev(c.qs[rev]), d=to_dev(c.d[rev]))
+    assert y.tobytes() == yr[rev].tobytes()
+
+
+@pytest.mark.parametrize("kind", ["e4m3", "blk128"])
+def test_gemv_matrix_core_padded_row_stride(fg, kind):
+    case(f"{kind} matrix cores, padded row stride")
+    out_f, in_f, m = 100, 1056, 5
+    c = Case(kind, out_f, in_f, m)
+    pad = 48
+    Wp = np.zeros((out_f, c.row_bytes + pad), dtype=np.uint8)
+    Wp[:, :c.row_bytes] = c.W
+    Wp[:, c.row_bytes:] = 0x7F  # NaN codes, never read
+    y = c.gpu(fg, Wd=to_dev(Wp), row_bytes=c.row_bytes + pad)
+    yo, A = c.oracle()
     _assert_close(y, yo, A)
 
 
@@ -226,7 +287,8 @@ def test_max_in_f(fg, kind):
 
 # The largest m the library accepts (the launch grid's y dimension indexes activation rows):
 # in_f = 256 takes the Q8_0 fast path, and m = 65535 is 8192 passes of 8 rows, the last one
-# with a single row.  Every output against the oracle, and sampled rows bit-identical to m=1.
+# with a single row.  Every output against the oracle, and sampled rows bit-identical to the
+# same row computed alone.
 @pytest.mark.parametrize("kind", KINDS)
 def test_max_m(fg, kind):
     m, out_f, in_f = 65535, 5, 256
@@ -236,8 +298,7 @@ def test_max_m(fg, kind):
     yo, A = c.oracle()
     _assert_close(y, yo, A)
     for t in (0, 1, 7, 8, 32767, m - 2, m - 1):
-        y1 = c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)
-        assert y1[0].tobytes() == y[t].tobytes(), f"row {t}"
+        assert row_reference(fg, c, t, m).tobytes() == y[t].tobytes(), f"row {t}"
 
 
 def test_bad_arguments_raise_and_launch_nothing(fg):
