@@ -22,7 +22,8 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 SOURCES = {
     "producer.hip": ["-ffp-contract=off"],
     "gemv_e4m3.hip": [],
-    "gemv_e4m3_mfma.hip": [],
+    # MFMA results straight into VGPRs (they feed VALU fmas; the AGPR form adds a copy each)
+    "gemv_e4m3_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemv_q8_0.hip": [],
     "read_ceiling.hip": [],
     "requant.hip": ["-ffp-contract=off"],

@@ -142,13 +142,14 @@ def test_gemv_sheet_shapes_every_row(fg, kind, out_f, in_f):
 
 
 def on_matrix_cores(kind, m, in_f):
-    """The e4m3 containers take the matrix-core kernel for m >= 5 up to in_f = 8192."""
-    return kind != "q8_0" and m >= 5 and in_f <= 8192
+    """The e4m3 containers take the matrix-core kernel for m >= 4 up to in_f = 8192."""
+    return kind != "q8_0" and m >= 4 and in_f <= 8192
 
 
 def row_reference(fg, c, t, m):
     """Row t of activation rows qs/d computed alone: an m = 1 call, or, where an m-row call
-    runs on the matrix cores, a 5-row call holding row t first and four other rows after it."""
+    runs on the matrix cores, a 5-row call holding row t first and four other rows after it
+    (so row t sits at another position among other rows)."""
     if not on_matrix_cores(c.kind, m, c.in_f):
         return c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)[0]
     idx = [t] + [(t + k) % c.m for k in range(1, 5)]
@@ -158,7 +159,7 @@ def row_reference(fg, c, t, m):
 # m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
 # m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.  Each row
 # of an m-row call is bit-identical to the same row computed alone: to an m = 1 call on the
-# vector path, and on the matrix cores (e4m3 containers, m >= 5, in_f <= 8192) to that row at
+# vector path, and on the matrix cores (e4m3 containers, m >= 4, in_f <= 8192) to that row at
 # another position among other rows.
 @pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("kind", KINDS)
@@ -183,7 +184,7 @@ MFMA_SHAPES = [(1, 32), (17, 288), (100, 1056), (200, 4128), (129, 8160), (65, 8
                (33, 8224), (300, 5120)]
 
 
-@pytest.mark.parametrize("m", [5, 8, 9, 16, 17])
+@pytest.mark.parametrize("m", [4, 5, 8, 9, 16, 17])
 @pytest.mark.parametrize("out_f,in_f", MFMA_SHAPES)
 @pytest.mark.parametrize("kind", ["e4m3", "blk128"])
 def test_gemv_matrix_core_shapes_match_oracle(fg, kind, out_f, in_f, m):
@@ -192,6 +193,28 @@ def test_gemv_matrix_core_shapes_match_oracle(fg, kind, out_f, in_f, m):
     y = c.gpu(fg)
     yo, A = c.oracle()
     _assert_close(y, yo, A)
+
+
+# Beyond the matrix-core kernel's limits (in_f > 8192, or a row stride of 64 MiB or more, where
+# 16 rows' offsets would leave 32 bits) several rows take the vector path, bit-identical to m=1.
+@pytest.mark.parametrize("kind", ["e4m3", "blk128"])
+def test_gemv_vector_path_beyond_the_matrix_core_limits(fg, kind):
+    case(f"{kind} m=8 with a 64 MiB row stride")
+    out_f, in_f, m = 3, 256, 8
+    c = Case(kind, out_f, in_f, m)
+    rb = (1 << 26) + 16
+    flat = torch.zeros((out_f - 1) * rb + in_f, dtype=torch.uint8, device=dev())
+    for r in range(out_f):
+        flat[r * rb:r * rb + in_f] = torch.from_numpy(c.W[r]).to(dev())
+    y = c.gpu(fg, Wd=flat, row_bytes=rb)
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+    for t in range(m):
+        y1 = c.gpu(fg, Wd=flat, row_bytes=rb, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)
+        assert y[t].tobytes() == y1[0].tobytes(), t
+    assert fg.gemv_launch_info(kind, rb, m, in_f, out_f)["kernel"].startswith("k_gemv_e4m3<")
+    assert fg.gemv_launch_info(kind, in_f, m, in_f, out_f)["kernel"].startswith("k_gemv_e4m3_mfma<")
+    assert fg.gemv_launch_info(kind, 8224, m, 8224, out_f)["kernel"].startswith("k_gemv_e4m3<")
 
 
 @pytest.mark.parametrize("kind", ["e4m3", "blk128"])
