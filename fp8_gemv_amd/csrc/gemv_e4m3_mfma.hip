@@ -60,26 +60,26 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRowsPerWave = 16;                    // the MFMA's M
-constexpr int kWavesM = 4;                          // waves per workgroup
-constexpr int kThreadsM = kWavesM * kWave;
 constexpr int kMT = 8;                              // activation rows per workgroup
 constexpr uint32_t kPastEnd = 0x80000000u;  // an offset past every resource used here
-constexpr int kMaxInFM = 8192;              // widest row this path takes
 
 // A step is 16 rows x step_cols(R) columns, loaded R rows per wave-wide load.
 __host__ __device__ constexpr int step_cols(int R) { return 1024 / R; }
-// relay row pitch: 16 rows' 8-byte fragment reads then fall on distinct bank pairs
-__host__ __device__ constexpr int relay_pitch(int R) { return step_cols(R) + (R == 4 ? 32 : 16); }
+// relay row pitch: a row starts 4 banks after the previous one, so the 16 rows' 32-byte
+// fragment reads cover every bank exactly twice (the two passes a 512-byte read needs anyway)
+__host__ __device__ constexpr int relay_pitch(int R) { return step_cols(R) + 16; }
 // per wave: 16 weight rows, 8 activation rows, 8 x (step_cols / 32) scales
 __host__ __device__ constexpr int relay_bytes(int R) {
   return (kRowsPerWave + kMT) * relay_pitch(R) + kMT * (step_cols(R) / 32) * 4;
 }
 
-// U steps in flight, WPE waves per SIMD, R rows per load, KS waves per 16-row group.
-template <int U_, int WPE_, int R_, int KS_>
+// U steps in flight, WPE waves per SIMD, R rows per load, KS waves per 16-row group, WAVES
+// waves per workgroup.
+template <int U_, int WPE_, int R_, int KS_, int WAVES_>
 struct MCfg {
-  static constexpr int U = U_, WPE = WPE_, R = R_, KS = KS_;
-  static constexpr int ROWS = kRowsPerWave * kWavesM / KS_;  // rows per workgroup
+  static constexpr int U = U_, WPE = WPE_, R = R_, KS = KS_, WAVES = WAVES_;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int ROWS = kRowsPerWave * WAVES / KS;  // rows per workgroup
 };
 
 // 8 e4m3 bytes -> 8 f16 (exact).
@@ -118,7 +118,7 @@ __device__ __forceinline__ half8_t act8(int2_t uu) {
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 template <bool BLK, class C>
-__global__ __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void k_gemv_e4m3_mfma(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
                       const float *__restrict__ grid, int grid_cols,
                       const int8_t *__restrict__ qs, const float *__restrict__ d,
@@ -126,8 +126,9 @@ void k_gemv_e4m3_mfma(const uint8_t *__restrict__ W, int64_t row_bytes, float sc
   constexpr int U = C::U, R = C::R, KS = C::KS;
   constexpr int SC = step_cols(R), NQ = kRowsPerWave / R, RP = relay_pitch(R), KB = SC / 32;
   static_assert(128 % C::ROWS == 0, "a workgroup's rows lie in one 128-row tile");
+  static_assert(C::WAVES % KS == 0, "a workgroup holds whole row groups");
   static_assert(KB % 4 == 0, "a step covers whole 128-column tiles");
-  __shared__ __align__(16) unsigned char relay[kWavesM * relay_bytes(R)];
+  __shared__ __align__(16) unsigned char relay[C::WAVES * relay_bytes(R)];
 
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
@@ -273,46 +274,59 @@ hipError_t launch_m(const uint8_t *W, int64_t row_bytes, float scale, const floa
                     int grid_cols, const int8_t *qs, const float *d, float *y, int m, int in_f,
                     int out_f, hipStream_t s) {
   const dim3 g((out_f + C::ROWS - 1) / C::ROWS, (m + kMT - 1) / kMT);
-  hipLaunchKernelGGL((k_gemv_e4m3_mfma<BLK, C>), g, dim3(kThreadsM), 0, s, W, row_bytes, scale,
+  hipLaunchKernelGGL((k_gemv_e4m3_mfma<BLK, C>), g, dim3(C::THREADS), 0, s, W, row_bytes, scale,
                      grid, grid_cols, qs, d, y, m, in_f, out_f);
   return hipGetLastError();
 }
 
-using MCfgDefault = MCfg<1, 6, 4, 4>;
+// Measured at 17408 x 5120 and 5120 x 17408 (m = 4 and 8): one step in flight, 4 waves per
+// row group; rows of more than 8192 columns split 8 ways in 8-wave workgroups, so that the
+// few long rows still give enough waves.
+using MCfgSmall = MCfg<1, 6, 4, 4, 4>;  // in_f <= 8192
+using MCfgLong = MCfg<1, 6, 4, 8, 8>;   // in_f > 8192
+
+template <class F>
+auto with_mcfg(int in_f, F &&f) {
+  return in_f <= 8192 ? f(Tag<MCfgSmall>{}) : f(Tag<MCfgLong>{});
+}
 
 }  // namespace
 
 bool gemv_e4m3_mfma_applies(int64_t row_bytes, int m, int in_f) {
-  // offsets of the wave's 16 rows and of 16 activation rows stay below the past-the-end offset
-  return m >= 4 && in_f <= kMaxInFM && row_bytes <= ((int64_t)1 << 26);
+  (void)in_f;
+  // offsets of the wave's 16 rows stay below the past-the-end offset
+  return m >= 3 && row_bytes <= ((int64_t)1 << 26);
 }
 
 hipError_t launch_gemv_e4m3_mfma(const uint8_t *W, int64_t row_bytes, float scale,
                                  const float *grid, int grid_cols, bool blk128, const int8_t *qs,
                                  const float *d, float *y, int m, int in_f, int out_f,
                                  hipStream_t s) {
-  if (blk128)
-    return launch_m<true, MCfgDefault>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f,
-                                       out_f, s);
-  return launch_m<false, MCfgDefault>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f,
-                                      out_f, s);
+  return with_mcfg(in_f, [&](auto tag) {
+    using C = typename decltype(tag)::type;
+    if (blk128)
+      return launch_m<true, C>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+    return launch_m<false, C>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
+  });
 }
 
 LaunchDesc describe_gemv_e4m3_mfma(bool blk128, int m, int in_f, int out_f) {
-  LaunchDesc r;
-  r.grid_x = (unsigned)((out_f + MCfgDefault::ROWS - 1) / MCfgDefault::ROWS);
-  r.grid_y = (unsigned)((m + kMT - 1) / kMT);
-  r.threads = kThreadsM;
-  r.lds = 0;  // static: the relays only
-  r.kernel = blk128 ? "k_gemv_e4m3_mfma<true" : "k_gemv_e4m3_mfma<false";
-  static const std::string text = [] {
-    char b[64];
-    snprintf(b, sizeof b, "MCfg<%d, %d, %d, %d>", MCfgDefault::U, MCfgDefault::WPE,
-             MCfgDefault::R, MCfgDefault::KS);
-    return std::string(b);
-  }();
-  r.config = text.c_str();
-  return r;
+  return with_mcfg(in_f, [&](auto tag) {
+    using C = typename decltype(tag)::type;
+    LaunchDesc r;
+    r.grid_x = (unsigned)((out_f + C::ROWS - 1) / C::ROWS);
+    r.grid_y = (unsigned)((m + kMT - 1) / kMT);
+    r.threads = C::THREADS;
+    r.lds = 0;  // static: the relays only
+    r.kernel = blk128 ? "k_gemv_e4m3_mfma<true" : "k_gemv_e4m3_mfma<false";
+    static const std::string text = [] {
+      char b[64];
+      snprintf(b, sizeof b, "MCfg<%d, %d, %d, %d, %d>", C::U, C::WPE, C::R, C::KS, C::WAVES);
+      return std::string(b);
+    }();
+    r.config = text.c_str();
+    return r;
+  });
 }
 
 }  // namespace fp8gemv

@@ -172,10 +172,10 @@ int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const floa
  *   row_bytes  >= in_f, multiple of 16;  W 16-byte aligned
  *   scale      per-tensor dequantisation factor, applied once per output
  *   qs, d, y   as for gemv_q8_0_q81
- * Each activation row is computed independently.  For m <= 3, or in_f > 8192, row t of an
- * m-row call is bit-identical to an m=1 call on that row.  For 4 <= m and in_f <= 8192 the
+ * Each activation row is computed independently.  For m <= 2 (or a row_bytes of 64 MiB or
+ * more) row t of an m-row call is bit-identical to an m=1 call on that row.  For m >= 3 the
  * products run on the matrix cores with a different (fixed) summation order: row t is then
- * bit-identical to the same row in any other call with m >= 4, whatever its position and the
+ * bit-identical to the same row in any other call with m >= 3, whatever its position and the
  * other rows, and agrees with m=1 to rounding.
  */
 int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,

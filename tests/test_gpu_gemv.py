@@ -142,8 +142,8 @@ def test_gemv_sheet_shapes_every_row(fg, kind, out_f, in_f):
 
 
 def on_matrix_cores(kind, m, in_f):
-    """The e4m3 containers take the matrix-core kernel for m >= 4 up to in_f = 8192."""
-    return kind != "q8_0" and m >= 4 and in_f <= 8192
+    """The e4m3 containers take the matrix-core kernel for m >= 3."""
+    return kind != "q8_0" and m >= 3
 
 
 def row_reference(fg, c, t, m):
@@ -159,8 +159,8 @@ def row_reference(fg, c, t, m):
 # m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
 # m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.  Each row
 # of an m-row call is bit-identical to the same row computed alone: to an m = 1 call on the
-# vector path, and on the matrix cores (e4m3 containers, m >= 4, in_f <= 8192) to that row at
-# another position among other rows.
+# vector path, and on the matrix cores (e4m3 containers, m >= 3) to that row at another
+# position among other rows.
 @pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("kind", KINDS)
 def test_gemv_m_rows_bit_identical_per_row(fg, kind, out_f, in_f):
@@ -177,14 +177,16 @@ def test_gemv_m_rows_bit_identical_per_row(fg, kind, out_f, in_f):
 
 
 # The matrix-core kernel at its edges: in_f not a multiple of its 256-column step or of the
-# 1 KiB group of 4 steps, in_f = 8192 (its largest) and 8224 (the vector path again), out_f
-# not a multiple of a wave's 16 rows or a workgroup's 64, block-128 grids with several row
-# tiles, m = 8 (one full pass), 9 and 17 (a last pass of one row), 16 (two full passes).
+# 1 KiB span of the 4 waves that share a row group (so some waves have no columns), rows
+# from one step to 65536 columns, out_f not a multiple of a wave's 16 rows, block-128 grids
+# with several row tiles, m = 3 (the smallest it takes), 8 (one full pass), 9 and 17 (a last
+# pass of one row), 16 (two full passes).  Rows of more than 8192 columns take the 8-way
+# column split.
 MFMA_SHAPES = [(1, 32), (17, 288), (100, 1056), (200, 4128), (129, 8160), (65, 8192),
-               (33, 8224), (300, 5120)]
+               (33, 8224), (300, 5120), (40, 17408), (9, 65536)]
 
 
-@pytest.mark.parametrize("m", [4, 5, 8, 9, 16, 17])
+@pytest.mark.parametrize("m", [3, 5, 8, 9, 16, 17])
 @pytest.mark.parametrize("out_f,in_f", MFMA_SHAPES)
 @pytest.mark.parametrize("kind", ["e4m3", "blk128"])
 def test_gemv_matrix_core_shapes_match_oracle(fg, kind, out_f, in_f, m):
@@ -195,8 +197,8 @@ def test_gemv_matrix_core_shapes_match_oracle(fg, kind, out_f, in_f, m):
     _assert_close(y, yo, A)
 
 
-# Beyond the matrix-core kernel's limits (in_f > 8192, or a row stride of 64 MiB or more, where
-# 16 rows' offsets would leave 32 bits) several rows take the vector path, bit-identical to m=1.
+# Beyond the matrix-core kernel's limit (a row stride of 64 MiB or more, where 16 rows'
+# offsets would leave 32 bits) several rows take the vector path, bit-identical to m=1.
 @pytest.mark.parametrize("kind", ["e4m3", "blk128"])
 def test_gemv_vector_path_beyond_the_matrix_core_limits(fg, kind):
     case(f"{kind} m=8 with a 64 MiB row stride")
@@ -214,7 +216,8 @@ def test_gemv_vector_path_beyond_the_matrix_core_limits(fg, kind):
         assert y[t].tobytes() == y1[0].tobytes(), t
     assert fg.gemv_launch_info(kind, rb, m, in_f, out_f)["kernel"].startswith("k_gemv_e4m3<")
     assert fg.gemv_launch_info(kind, in_f, m, in_f, out_f)["kernel"].startswith("k_gemv_e4m3_mfma<")
-    assert fg.gemv_launch_info(kind, 8224, m, 8224, out_f)["kernel"].startswith("k_gemv_e4m3<")
+    assert fg.gemv_launch_info(kind, 65536, m, 65536, out_f)["kernel"].startswith("k_gemv_e4m3_mfma<")
+    assert fg.gemv_launch_info(kind, in_f, 2, in_f, out_f)["kernel"].startswith("k_gemv_e4m3<")
 
 
 @pytest.mark.parametrize("kind", ["e4m3", "blk128"])
