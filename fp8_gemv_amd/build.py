@@ -25,6 +25,7 @@ SOURCES = {
     # MFMA results straight into VGPRs (they feed VALU fmas; the AGPR form adds a copy each)
     "gemv_e4m3_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemv_q8_0.hip": [],
+    "gemv_q8_0_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "read_ceiling.hip": [],
     "requant.hip": ["-ffp-contract=off"],
     "capi.hip": [],

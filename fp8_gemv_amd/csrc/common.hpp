@@ -158,6 +158,13 @@ hipError_t launch_gemv_e4m3_mfma(const uint8_t *W, int64_t row_bytes, float scal
                                  const float *d, float *y, int m, int in_f, int out_f,
                                  hipStream_t s);
 LaunchDesc describe_gemv_e4m3_mfma(bool blk128, int m, int in_f, int out_f);
+// The matrix-core kernel for several activation rows over Q8_0 (gemv_q8_0_mfma.hip);
+// launch_gemv_q8_0 and describe_gemv_q8_0 choose it where gemv_q8_0_mfma_applies.
+bool gemv_q8_0_mfma_applies(const uint8_t *W, int64_t row_bytes, int m, int in_f);
+hipError_t launch_gemv_q8_0_mfma(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
+                                 const float *d, float *y, int m, int in_f, int out_f,
+                                 hipStream_t s);
+LaunchDesc describe_gemv_q8_0_mfma(int m, int in_f, int out_f);
 LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f);
 hipError_t launch_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                                int grid_cols, bool blk128, void *Wq, int64_t q_row_bytes,

@@ -157,8 +157,12 @@ int gated_rmsnorm_q8_1(const float *o, const float *g, const float *w, float *z,
  *   y          f32 [m, out_f]
  * Alignment: W and row_bytes 2-byte aligned; the fast path also needs W 16-byte aligned,
  * row_bytes % 16 == 0 and in_f % 256 == 0, otherwise a slower path runs.  qs, d 16-byte
- * aligned.  Each activation row is computed independently: row t of an m-row call is
- * bit-identical to an m=1 call on that row.
+ * aligned.  Each activation row is computed independently.  Every block's integer sum is
+ * exact.  For m <= 2, off the fast path, or with a row_bytes of 64 MiB or more, row t of an
+ * m-row call is bit-identical to an m=1 call on that row.  For m >= 3 on the fast path the
+ * products run on the matrix cores and the scaling follows a different (fixed) order: row t
+ * is then bit-identical to the same row in any other such call, whatever its position and
+ * the other rows, and agrees with m=1 to rounding.
  */
 int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
                   int m, int in_f, int out_f, void *stream);

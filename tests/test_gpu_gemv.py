@@ -142,8 +142,9 @@ def test_gemv_sheet_shapes_every_row(fg, kind, out_f, in_f):
 
 
 def on_matrix_cores(kind, m, in_f):
-    """The e4m3 containers take the matrix-core kernel for m >= 3."""
-    return kind != "q8_0" and m >= 3
+    """Several activation rows (m >= 3) take the matrix-core kernels: always for the e4m3
+    containers, and for Q8_0 on its fast-path rows (in_f % 256 == 0, aligned rows)."""
+    return m >= 3 and (kind != "q8_0" or in_f % 256 == 0)
 
 
 def row_reference(fg, c, t, m):
@@ -159,8 +160,8 @@ def row_reference(fg, c, t, m):
 # m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
 # m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.  Each row
 # of an m-row call is bit-identical to the same row computed alone: to an m = 1 call on the
-# vector path, and on the matrix cores (e4m3 containers, m >= 3) to that row at another
-# position among other rows.
+# vector path, and on the matrix cores (m >= 3) to that row at another position among other
+# rows.
 @pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("kind", KINDS)
 def test_gemv_m_rows_bit_identical_per_row(fg, kind, out_f, in_f):
@@ -197,30 +198,52 @@ def test_gemv_matrix_core_shapes_match_oracle(fg, kind, out_f, in_f, m):
     _assert_close(y, yo, A)
 
 
-# Beyond the matrix-core kernel's limit (a row stride of 64 MiB or more, where 16 rows'
+# The Q8_0 matrix-core kernel (fast-path rows: in_f a multiple of the 8-block group): one
+# group up to 65536 columns, groups that do not divide evenly between the waves of a row
+# group (1280 = 5 groups over 4 waves, 4352 = 17, 8448 = 33 over 8), out_f not a multiple of
+# 16, rows past 8192 columns split 8 ways.
+Q8_MFMA_SHAPES = [(1, 256), (17, 512), (100, 1280), (200, 4352), (65, 8192), (33, 8448),
+                  (300, 5120), (40, 17408), (9, 65536)]
+
+
+@pytest.mark.parametrize("m", [3, 5, 8, 9, 16, 17])
+@pytest.mark.parametrize("out_f,in_f", Q8_MFMA_SHAPES)
+def test_gemv_q8_0_matrix_core_shapes_match_oracle(fg, out_f, in_f, m):
+    case(f"q8_0 matrix cores out_f={out_f} in_f={in_f} m={m}")
+    c = Case("q8_0", out_f, in_f, m)
+    y = c.gpu(fg)
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+
+
+# Beyond the matrix-core kernels' limit (a row stride of 64 MiB or more, where 16 rows'
 # offsets would leave 32 bits) several rows take the vector path, bit-identical to m=1.
-@pytest.mark.parametrize("kind", ["e4m3", "blk128"])
+@pytest.mark.parametrize("kind", KINDS)
 def test_gemv_vector_path_beyond_the_matrix_core_limits(fg, kind):
     case(f"{kind} m=8 with a 64 MiB row stride")
     out_f, in_f, m = 3, 256, 8
     c = Case(kind, out_f, in_f, m)
     rb = (1 << 26) + 16
-    flat = torch.zeros((out_f - 1) * rb + in_f, dtype=torch.uint8, device=dev())
+    nbytes = c.W.shape[1]
+    flat = torch.zeros((out_f - 1) * rb + nbytes, dtype=torch.uint8, device=dev())
     for r in range(out_f):
-        flat[r * rb:r * rb + in_f] = torch.from_numpy(c.W[r]).to(dev())
+        flat[r * rb:r * rb + nbytes] = torch.from_numpy(c.W[r]).to(dev())
     y = c.gpu(fg, Wd=flat, row_bytes=rb)
     yo, A = c.oracle()
     _assert_close(y, yo, A)
     for t in range(m):
         y1 = c.gpu(fg, Wd=flat, row_bytes=rb, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)
         assert y[t].tobytes() == y1[0].tobytes(), t
-    assert fg.gemv_launch_info(kind, rb, m, in_f, out_f)["kernel"].startswith("k_gemv_e4m3<")
-    assert fg.gemv_launch_info(kind, in_f, m, in_f, out_f)["kernel"].startswith("k_gemv_e4m3_mfma<")
-    assert fg.gemv_launch_info(kind, 65536, m, 65536, out_f)["kernel"].startswith("k_gemv_e4m3_mfma<")
-    assert fg.gemv_launch_info(kind, in_f, 2, in_f, out_f)["kernel"].startswith("k_gemv_e4m3<")
+    vec, mat = (("k_gemv_q8_0_fast", "k_gemv_q8_0_mfma") if kind == "q8_0"
+                else ("k_gemv_e4m3<", "k_gemv_e4m3_mfma<"))
+    rbf = (lambda n: n // 32 * 34) if kind == "q8_0" else (lambda n: n)
+    assert fg.gemv_launch_info(kind, rb, m, in_f, out_f)["kernel"].startswith(vec)
+    assert fg.gemv_launch_info(kind, rbf(in_f), m, in_f, out_f)["kernel"].startswith(mat)
+    assert fg.gemv_launch_info(kind, rbf(65536), m, 65536, out_f)["kernel"].startswith(mat)
+    assert fg.gemv_launch_info(kind, rbf(in_f), 2, in_f, out_f)["kernel"].startswith(vec)
 
 
-@pytest.mark.parametrize("kind", ["e4m3", "blk128"])
+@pytest.mark.parametrize("kind", KINDS)
 def test_gemv_matrix_core_rows_independent_of_order(fg, kind):
     # the same 8 rows in reverse order give each row the same bits
     case(f"{kind} matrix cores, rows reversed")
@@ -231,10 +254,10 @@ def test_gemv_matrix_core_rows_independent_of_order(fg, kind):
     assert y.tobytes() == yr[rev].tobytes()
 
 
-@pytest.mark.parametrize("kind", ["e4m3", "blk128"])
+@pytest.mark.parametrize("kind", KINDS)
 def test_gemv_matrix_core_padded_row_stride(fg, kind):
     case(f"{kind} matrix cores, padded row stride")
-    out_f, in_f, m = 100, 1056, 5
+    out_f, in_f, m = 100, (1024 if kind == "q8_0" else 1056), 5
     c = Case(kind, out_f, in_f, m)
     pad = 48
     Wp = np.zeros((out_f, c.row_bytes + pad), dtype=np.uint8)
