@@ -25,9 +25,10 @@
 //   * The chunks go to a per-wave LDS relay in row order (pitch 272: a row starts 4 banks
 //     after the previous one).  The A fragment of block k is read straight from the raw rows:
 //     lane (i, g) takes 8 quants of row i at byte 34k + 2 + 8g (a 2-byte-aligned 8-byte LDS
-//     read).  The 128 fp16 block scales of the step are converted to f32 by a small pass into
-//     a [block][row] table, so a lane reads the 4 scales of its output rows with one 16-byte
-//     LDS read.
+//     read).  A group's block k has its fp16 scale at byte 2k of chunk 2k, so the lanes that
+//     load chunks 0, 2, .., 14 also convert that scale to f32 and write it to a [block][row]
+//     table next to the relay (which dword and which half are fixed per lane); a lane then
+//     reads the 4 scales of its output rows with one 16-byte LDS read.
 //   * The activation rows come straight from the q8_1 rows, as in the e4m3 kernel: per step
 //     two 16-byte loads per lane cover 8 rows x 256 columns, plus one block scale per lane,
 //     issued together with the step's weights, through a second small relay.  The int8 values
@@ -61,7 +62,8 @@ constexpr int kRelayA = kRowsPerWave * kAPitch;
 constexpr int kRelayB = kMT * kBPitch;
 constexpr int kRelayD = kMT * kGrpBlocks * 4;
 constexpr int kRelayW = kGrpBlocks * kRowsPerWave * 4;
-constexpr int kRelayBytes = kRelayA + kRelayB + kRelayD + kRelayW;
+constexpr int kRelaySink = 16;  // takes the writes of lanes with nothing to write
+constexpr int kRelayBytes = kRelayA + kRelayB + kRelayD + kRelayW + kRelaySink;
 static_assert(kRelayA % 16 == 0 && kRelayB % 16 == 0 && kRelayD % 16 == 0 &&
                   kRelayBytes % 16 == 0, "16-byte aligned relay parts");
 
@@ -108,17 +110,26 @@ void k_gemv_q8_0_mfma(const uint8_t *__restrict__ W, int64_t row_bytes,
   unsigned char *rb = rl + kRelayA;                  // activation: 8 rows of kBPitch
   float *rd = reinterpret_cast<float *>(rb + kRelayB);  // activation scales [8][8]
   float *rw = rd + kMT * kGrpBlocks;                    // weight scales [8 blocks][16 rows]
-  // load q, lane l: chunk 64q + l of the step's 16 x 17 (row-major); lanes past the 272
-  // chunks load nothing and park their relay write in the weight-scale table, which is
-  // rewritten later in the same step
-  uint32_t woff[kLoads], aoff[kLoads];
+  // load q, lane l: chunk c = 64q + l of the step's 16 x 17 (row-major), written to the
+  // relay at 16c (the pitch is 17 chunks).  Lanes past the 272 chunks load nothing; their
+  // writes land in the activation relay, which is written after them.  A lane whose chunk is
+  // 2k (k < 8) holds the fp16 scale of block k at byte 2k (quadword k / 4, bit 16 (k % 4));
+  // it writes that scale as f32 to the table, the others write to the sink.
+  constexpr uint32_t kSink = kRelayA + kRelayB + kRelayD + kRelayW;
+  static_assert(kAPitch == kGrpChunks * 16, "relay offset of chunk c is 16 c");
+  uint32_t woff[kLoads], soff[kLoads], sbit[kLoads];
+  bool shi[kLoads];
 #pragma unroll
   for (int q = 0; q < kLoads; ++q) {
     const int c = kWave * q + lane;
     const bool ok = c < kRowsPerWave * kGrpChunks;
     const int row = c / kGrpChunks, ch = c % kGrpChunks;
     woff[q] = ok ? (uint32_t)((int64_t)row * row_bytes + 16 * ch) : kPastEnd;
-    aoff[q] = ok ? (uint32_t)(row * kAPitch + 16 * ch) : (uint32_t)(kRelayA + kRelayB + kRelayD);
+    const bool sc = ok && ch % 2 == 0 && ch < 2 * kGrpBlocks;
+    const int k = ch / 2;
+    soff[q] = sc ? (uint32_t)(kRelayA + kRelayB + kRelayD + (k * kRowsPerWave + row) * 4) : kSink;
+    sbit[q] = 16u * (uint32_t)(k % 4);
+    shi[q] = k >= 4;
   }
   // Activation rows [t0, t0 + nt): lane l loads 32 bytes of row l / 8 at step column
   // 32 (l % 8) and the scale of that block; rows past nt read zeros.
@@ -154,21 +165,19 @@ void k_gemv_q8_0_mfma(const uint8_t *__restrict__ W, int64_t row_bytes,
   for (int s = sbeg; s < sbeg + nmine; ++s) {
     wave_lds_fence();
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) *reinterpret_cast<int4_t *>(rl + aoff[q]) = st.w[q];
+    for (int q = 0; q < kLoads; ++q) {
+      const int4_t w = st.w[q];
+      *reinterpret_cast<int4_t *>(rl + 16 * (kWave * q + lane)) = w;
+      const uint64_t lo = (uint64_t)(uint32_t)w[0] | ((uint64_t)(uint32_t)w[1] << 32);
+      const uint64_t hi = (uint64_t)(uint32_t)w[2] | ((uint64_t)(uint32_t)w[3] << 32);
+      const uint16_t h = (uint16_t)((shi[q] ? hi : lo) >> sbit[q]);
+      *reinterpret_cast<float *>(rl + soff[q]) = (float)__builtin_bit_cast(_Float16, h);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       *reinterpret_cast<int4_t *>(rb + arw * kBPitch + 32 * apc + 16 * h) = st.a[h];
     rd[arw * kGrpBlocks + apc] = st.sc;
     load_step(st, s + 1);
-    wave_lds_fence();
-    // the step's 128 weight scales: lane l converts (block, row) = (l / 16, l % 16) and
-    // (l / 16 + 4, l % 16)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int k = lane / 16 + 4 * e, row = lane % 16;
-      const _Float16 h = *reinterpret_cast<const _Float16 *>(rl + row * kAPitch + 34 * k);
-      rw[k * kRowsPerWave + row] = (float)h;
-    }
     wave_lds_fence();
 #pragma unroll
     for (int k = 0; k < kGrpBlocks; ++k) {
