@@ -75,26 +75,26 @@ __device__ __forceinline__ double lane_f64(double v, int lane) {
 }
 
 // 1 / sqrt(mean(x^2) + eps) for one row, computed by the whole workgroup; every thread
-// returns the same value.  `red` is LDS scratch for 2 doubles per wave.
-__device__ double row_scale(const float *__restrict__ x, int ncols, float eps, double *red) {
+// returns the same value.  `red` is LDS scratch for 2 doubles per wave.  Inlined, so that the
+// loads below stay in the kernel's own instruction stream.
+__device__ __forceinline__ double row_scale(const float *__restrict__ x, int ncols, float eps,
+                                            double *red) {
   double hi = 0.0, lo = 0.0;
   constexpr int kBatch = 8;  // loads issued together before they are accumulated
   // Batches of kBatch loads; the next batch is issued before the current one is accumulated,
-  // so a long row costs one load latency, not one per batch.  The elements are accumulated
-  // in the same order either way.
+  // so a long row costs one load latency, not one per batch.  Every thread runs the same
+  // number of batches, and a load past the row reads zeros through the buffer resource's
+  // range check, so there is no branch around any load and the compiler waits only for the
+  // batch it uses.  A zero adds nothing (TwoSum of hi and 0 is exactly hi and 0), so the sum
+  // is that of the row's own elements, in the same per-thread order.
+  const rsrc_t xrs = buf_rsrc(x, (uint32_t)ncols * 4);
   auto load_batch = [&](float4 (&v)[kBatch], int base) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int j = base + u * kColsPerPass;
-      v[u] = j < ncols ? *reinterpret_cast<const float4 *>(x + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int u = 0; u < kBatch; ++u)
+      v[u] = __builtin_bit_cast(float4, buf_load16(xrs, (uint32_t)(base + u * kColsPerPass) * 4));
   };
-  float4 v[kBatch];
-  load_batch(v, threadIdx.x * 4);
-  for (int base = threadIdx.x * 4; base < ncols; base += kBatch * kColsPerPass) {
-    float4 nv[kBatch];
-    const int next = base + kBatch * kColsPerPass;
-    if (next < ncols) load_batch(nv, next);
+  const int nbatch = (ncols + kBatch * kColsPerPass - 1) / (kBatch * kColsPerPass);
+  auto accumulate = [&](const float4 (&v)[kBatch]) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -107,8 +107,19 @@ __device__ double row_scale(const float *__restrict__ x, int ncols, float eps, d
         lo += e;
       }
     }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) v[u] = nv[u];
+  };
+  // Two buffers used in turn (no register copies between batches, which would make the
+  // compiler wait for the batch just issued).  Past the last batch every offset lies past
+  // the row: zeros, and no memory traffic.
+  const int t4 = threadIdx.x * 4;
+  float4 va[kBatch], vb[kBatch];
+  load_batch(va, t4);
+  for (int b = 0; b < nbatch; b += 2) {
+    load_batch(vb, t4 + (b + 1) * kBatch * kColsPerPass);
+    accumulate(va);
+    if (b + 1 >= nbatch) break;
+    load_batch(va, t4 + (b + 2) * kBatch * kColsPerPass);
+    accumulate(vb);
   }
   // Across the wave: DPP within each row of 16 lanes (quad swaps, then rotations by 4 and
   // 8), then the four row sums from lanes 0, 16, 32, 48 added in that fixed order.  Lanes of
