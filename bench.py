@@ -417,6 +417,77 @@ def summarize_sq(csv_paths) -> str:
     return "\n".join(lines)
 
 
+def summarize_mem(csv_paths) -> str:
+    """Median per-dispatch L2 (TCC), L1 (TCP) and address-unit (TA) counters per m = 1 GEMV
+    launch and per row-pattern read kernel, over one or more rocprofv3 --pmc passes:
+
+      DRAM MB      = TCC_EA0_RDREQ_sum x 128: each memory read request of these cold streams
+                     fetches one 128-byte line (the GEMVs read 8.0 requests per KiB);
+      L1->L2 per DRAM rd = TCP_TCC_READ_REQ_sum / TCC_EA0_RDREQ_sum: how often the same line is
+                     asked of the L2 (1.0: once per line fetched from memory);
+
+    and, for the GEMVs, the same counters per KiB of the launch's weight bytes:
+
+      L2 req/KiB   = TCC_REQ_sum: requests that reach the L2 (any size);
+      DRAM rd/KiB  = TCC_EA0_RDREQ_sum: L2 read requests to memory, and the share of them that
+                     are 32-byte (TCC_EA0_RDREQ_32B_sum) rather than 64-byte requests;
+      L2 hit %     = TCC_HIT_sum over TCC_HIT_sum + TCC_MISS_sum;
+      L1->L2/KiB   = TCP_TCC_READ_REQ_sum, and its mean latency in cycles per request
+                     (TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum).
+    """
+    import csv
+    import statistics
+    vals = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            name, grid, wg = r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"])
+            if "k_read_rows" in name or "k_read_line_windows" in name:
+                label = "read"
+            elif "gemv" in name:
+                label = _label_of(name, grid, wg, int(r["LDS_Block_Size"]))
+                if label == "-":
+                    continue
+            else:
+                continue
+            key = (label, _kernel_key(name, grid, wg))
+            d = (path, r["Dispatch_Id"])
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], {})[d] = float(r["Counter_Value"])
+    med = {k: {c: statistics.median(v.values()) for c, v in cs.items()} for k, cs in vals.items()}
+
+    def kib(label):
+        arm, shape = label.split("@")
+        out_f, in_f = (int(x) for x in shape.split("x"))
+        return weight_bytes(arm, out_f, in_f) / 1024
+
+    derived = [
+        ("DRAM MB", lambda k, c: c["TCC_EA0_RDREQ_sum"] * 128 / 1e6),
+        ("L1->L2 per DRAM rd", lambda k, c: c["TCP_TCC_READ_REQ_sum"] / c["TCC_EA0_RDREQ_sum"]),
+        ("L2 req/KiB", lambda k, c: c["TCC_REQ_sum"] / kib(k[0])),
+        ("DRAM rd/KiB", lambda k, c: c["TCC_EA0_RDREQ_sum"] / kib(k[0])),
+        ("32B share %", lambda k, c: 100 * c["TCC_EA0_RDREQ_32B_sum"] / c["TCC_EA0_RDREQ_sum"]),
+        ("L2 hit %", lambda k, c: 100 * c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])),
+        ("L1->L2/KiB", lambda k, c: c["TCP_TCC_READ_REQ_sum"] / kib(k[0])),
+        ("L1->L2 latency", lambda k, c: c["TCP_TCC_READ_REQ_LATENCY_sum"] / c["TCP_TCC_READ_REQ_sum"]),
+    ]
+    counters = sorted({c for k in med for c in med[k]})
+    lines = ["| launch | kernel (grid = threads) | " + " | ".join(n for n, _ in derived) + " |",
+             "|---" * (len(derived) + 2) + "|"]
+    for k in sorted(med):
+        cells = []
+        for _, f in derived:
+            try:
+                cells.append(f"{f(k, med[k]):.2f}")
+            except (KeyError, ValueError, ZeroDivisionError):
+                cells.append("-")
+        lines.append(f"| {k[0]} | {k[1]} | " + " | ".join(cells) + " |")
+    lines += ["", "Raw medians per dispatch:", "",
+              "| launch | " + " | ".join(counters) + " |", "|---" * (len(counters) + 1) + "|"]
+    for k in sorted(med):
+        lines.append(f"| {k[0]} | " + " | ".join(
+            f"{med[k][c]:.0f}" if c in med[k] else "-" for c in counters) + " |")
+    return "\n".join(lines)
+
+
 def traffic_for(kernel_label: str):
     """HBM bytes per launch of a GEMV from the committed counter summary, or None when the
     summary is missing, does not cover this launch, or was taken on other kernel sources."""
@@ -460,12 +531,17 @@ def main() -> int:
                     help="print a markdown summary of rocprofv3 SQ/GRBM counter passes, exit")
     ap.add_argument("--no-sheets", action="store_true",
                     help="skip the 27B / 1.7B projection shape sheets")
+    ap.add_argument("--summarize-mem", nargs="+", metavar="COUNTER_CSV",
+                    help="print the L2 / L1 request counter summary of rocprofv3 --pmc passes")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print a markdown summary of a rocprofv3 kernel trace and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM byte-counter summary of two rocprofv3 --pmc runs, exit")
     args = ap.parse_args()
 
+    if args.summarize_mem:
+        print(summarize_mem(args.summarize_mem))
+        return 0
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
         return 0
