@@ -797,7 +797,9 @@ def main() -> int:
 
     # Load-time e4m3 -> Q8_0 requantiser (gemv_e4m3_bench.rs, QUESTION: the ship path's Q8_0
     # slab), per shape and scale kind: reads the e4m3 plane (and grid), writes the Q8_0 rows.
-    requant = {}
+    # Beside it, a plain device copy of the same e4m3 plane (same rotation): the read + write
+    # rate the requantiser is compared with (`pct_of_copy`: its bytes per us over the copy's).
+    requant, copy_rate = {}, {}
     if not args.kernels_only:
         for (out_f, in_f, a), obj in arm_objs.items():
             if a not in ("e4m3", "blk128"):
@@ -814,15 +816,24 @@ def main() -> int:
                 else:
                     fg.requant_e4m3_blk128_q8_0(obj.W[c], obj.row_bytes, obj.grids[c],
                                                 obj.grid_cols, Wq[i % 2], nbq, in_f, out_f)
-            g = capture(lambda: [rq(i) for i in range(n)])
-            g.replay()
-            us = timed(g.replay, n) * 1e3
+            us, _ = graph_us(rq, n)
             moved = weight_bytes("e4m3", out_f, in_f) + grid_bytes(a, out_f, in_f) + out_f * nbq
+            if (out_f, in_f) not in copy_rate:
+                nw = weight_bytes("e4m3", out_f, in_f)
+                dst = torch.empty(nw, dtype=torch.uint8, device=dev)
+                cus, _ = graph_us(lambda i, obj=obj, dst=dst: dst.copy_(
+                    obj.W[i % obj.copies].reshape(-1)[:nw]), n)
+                copy_rate[(out_f, in_f)] = (cus, 2 * nw / cus / 1e3)
+                del dst
+            cus, cgbs = copy_rate[(out_f, in_f)]
             requant[f"{a}@{out_f}x{in_f}"] = {"us": round(us, 3), "bytes": moved,
                                               "GBs": round(moved / us / 1e3, 1),
-                                              "pct_peak": round(100 * moved / us / 1e3 / HBM_PEAK_GBS, 1)}
-            log(f"requant {a:6s} {out_f}x{in_f}: {us:8.2f} us  {moved / us / 1e3:7.1f} GB/s")
-            del g, Wq
+                                              "pct_peak": round(100 * moved / us / 1e3 / HBM_PEAK_GBS, 1),
+                                              "copy_us": round(cus, 3), "copy_GBs": round(cgbs, 1),
+                                              "pct_of_copy": round(100 * moved / us / 1e3 / cgbs, 1)}
+            log(f"requant {a:6s} {out_f}x{in_f}: {us:8.2f} us  {moved / us / 1e3:7.1f} GB/s; "
+                f"copy of the plane {cus:.2f} us, {cgbs:.1f} GB/s")
+            del Wq
 
     # Achievable read ceiling: the library's streaming-read measurement kernels in every load
     # pattern, each over four sizes (26, 89, 178 and 356 MB; the Q8_0 rows pattern over the

@@ -217,8 +217,9 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
  *                unspecified)
  *   Wq           output rows of q_row_bytes bytes: only the first in_f / 32 * 34 bytes of each
  *                row are written; 2-byte aligned, q_row_bytes >= in_f / 32 * 34 and even; must
- *                not overlap W.  Wq 16-byte aligned with q_row_bytes % 16 == 0 and
- *                in_f % 256 == 0 is the fastest layout (and the one the fast GEMV path needs).
+ *                not overlap W.  Packed rows (q_row_bytes = in_f / 32 * 34) in a 16-byte
+ *                aligned Wq are the fastest layout; with in_f % 256 == 0 they are also the
+ *                layout the fast GEMV path needs.
  *   in_f         multiple of 32, <= FP8GEMV_MAX_IN_F;  out_f >= 1
  */
 int requant_e4m3_q8_0(const uint8_t *W, int64_t row_bytes, float scale, void *Wq,

@@ -93,6 +93,62 @@ def test_requant_padded_and_unaligned_rows_leave_padding_alone(fg):
         assert np.all(got[:, nb * 34:] == 0xAB)
 
 
+# Blocks are numbered across rows (block g is block g % nb of row g / nb), so a workgroup's 256
+# blocks can span many rows.  Padded input rows, packed and padded output rows, and every store
+# mode: 16-byte (packed, total blocks % 8 == 0), 2-byte runs (packed otherwise, or an output
+# only 2-byte aligned) and per-block stores (padded output).
+@pytest.mark.parametrize("out_f,in_f,pad", [(37, 96, 16), (131, 288, 48), (65, 8704, 16),
+                                            (300, 256, 32), (3, 32, 16)])
+@pytest.mark.parametrize("out_pad,offset", [(0, 0), (0, 2), (4, 0)])
+def test_requant_padded_input_rows_and_row_crossing_workgroups(fg, out_f, in_f, pad, out_pad,
+                                                                offset):
+    case(f"requant strided out_f={out_f} in_f={in_f} pad={pad} out_pad={out_pad} off={offset}")
+    nb = in_f // 32
+    W = synth.e4m3_weights(out_f, in_f + pad)
+    grid = synth.blk128_grid(out_f, in_f)
+    qrb = nb * 34 + out_pad
+    for kw in ({"scale": 0.3}, {"grid": grid}):
+        want = oracle.requant_q8_0(W, in_f + pad, in_f, out_f, q_row_bytes=qrb, **kw)
+        got = _run(fg, W, in_f, out_f, q_row_bytes=qrb, offset=offset, fill=0xAB, **kw)
+        assert np.array_equal(got[:, :nb * 34], want[:, :nb * 34]), list(kw)
+        assert np.all(got[:, nb * 34:] == 0xAB)
+
+
+def test_requant_launch_split_at_two_to_the_30_blocks(fg):
+    """A plane of more than 2^30 blocks is requantised in row ranges of 2^30 blocks (a multiple
+    of 128 rows, so the block-128 grid row of a range starts on its first tile).  in_f = 65536:
+    ranges of 524288 rows; the rows on both sides of the split, and the first and last rows, are
+    checked against the oracle, per 128-row tile (a row's bytes depend only on the row and on
+    its tile's grid value)."""
+    in_f, nb, split = 65536, 2048, 524288
+    out_f = split + 200
+    case(f"requant launch split out_f={out_f} in_f={in_f}")
+    base = synth.e4m3_weights(256, in_f)          # row r of the plane is base row r % 256
+    grid = synth.blk128_grid(out_f, in_f)
+    Wd = to_dev(base).repeat((out_f + 255) // 256, 1)[:out_f]
+    Wq = torch.empty((out_f, nb * 34), dtype=torch.uint8, device=dev())
+    check = [0, 1, split - 2, split - 1, split, split + 1, out_f - 1]
+    try:
+        for arm in ("scale", "grid"):
+            Wq.fill_(0xAB)
+            if arm == "scale":
+                fg.requant_e4m3_q8_0(Wd, in_f, 0.3, Wq, nb * 34, in_f, out_f)
+            else:
+                fg.requant_e4m3_blk128_q8_0(Wd, in_f, to_dev(grid), grid.shape[1], Wq, nb * 34,
+                                            in_f, out_f)
+            torch.cuda.synchronize()
+            for r in check:
+                t0 = r // 128 * 128
+                tile_rows = np.stack([base[(t0 + i) % 256] for i in range(128)])
+                kw = {"scale": 0.3} if arm == "scale" else {"grid": grid[t0 // 128:t0 // 128 + 1]}
+                want = oracle.requant_q8_0(tile_rows, in_f, in_f, 128, rows=(r - t0, r - t0 + 1),
+                                           **kw)[r - t0]
+                assert np.array_equal(host(Wq[r]), want), (arm, r)
+    finally:
+        del Wd, Wq
+        torch.cuda.empty_cache()
+
+
 def test_requant_special_blocks(fg):
     case("requant special blocks")
     in_f = 256
