@@ -14,9 +14,13 @@
 //
 // gfx950 design (the same frame as the e4m3 matrix-core kernel):
 //   * Each wave owns 16 consecutive weight rows (the MFMA's M) and a share of their columns:
-//     KS waves share a row group, and their partial sums meet in LDS and are added in part
-//     order.  Up to 8 activation rows per workgroup (grid.y = ceil(m / 8)) are the MFMA's N
-//     columns 0..7; columns 8..15 repeat them and are never stored.
+//     KS waves share a row group, taking its column steps in turn (wave p: steps p, p + KS,
+//     ..), so the KS waves read adjacent pieces of the same rows at about the same time and a
+//     128-byte line cut between two steps is still in L2 for the second one (with contiguous
+//     shares per wave, 23% more bytes came from memory than the plane holds; interleaved, 11%).
+//     Their partial sums meet in LDS and are added in part order.  Up to 8 activation rows
+//     per workgroup (grid.y = ceil(m / 8)) are the MFMA's N columns 0..7; columns 8..15
+//     repeat them and are never stored.
 //   * Weights stream in steps of one group (8 blocks = 272 bytes = 17 chunks of 16 bytes) of
 //     each of the 16 rows: chunk index 64q + lane of the 16 x 17 is loaded by lane `lane` of
 //     load q (5 loads, the last with 16 lanes), so 17 consecutive lanes read 272 contiguous
@@ -24,11 +28,14 @@
 //     out_f an offset lies outside the buffer resource and the load returns zeros.
 //   * The chunks go to a per-wave LDS relay in row order (pitch 272: a row starts 4 banks
 //     after the previous one).  The A fragment of block k is read straight from the raw rows:
-//     lane (i, g) takes 8 quants of row i at byte 34k + 2 + 8g (a 2-byte-aligned 8-byte LDS
-//     read).  A group's block k has its fp16 scale at byte 2k of chunk 2k, so the lanes that
+//     lane (i, g) takes 8 quants of row i at byte 34k + 2 + 8g (aligned reads, below).  A
+//     group's block k has its fp16 scale at byte 2k of chunk 2k, so the lanes that
 //     load chunks 0, 2, .., 14 also convert that scale to f32 and write it to a [block][row]
 //     table next to the relay (which dword and which half are fixed per lane); a lane then
-//     reads the 4 scales of its output rows with one 16-byte LDS read.
+//     reads the 4 scales of its output rows with one 16-byte LDS read.  Block k's quants start
+//     4-byte aligned for odd k and 2 bytes past a dword for even k, so the fragment is read as
+//     two aligned dwords, or as three funnel-shifted by 2 bytes: a 2-byte-aligned 8-byte LDS
+//     read is legal here but cost about a fifth of the kernel's time at 5120 x 17408.
 //   * The activation rows come straight from the q8_1 rows, as in the e4m3 kernel: per step
 //     two 16-byte loads per lane cover 8 rows x 256 columns, plus one block scale per lane,
 //     issued together with the step's weights, through a second small relay.  The int8 values
@@ -97,9 +104,7 @@ void k_gemv_q8_0_mfma(const uint8_t *__restrict__ W, int64_t row_bytes,
   const int r0 = blockIdx.x * C::ROWS + (wave / KS) * kRowsPerWave;  // first weight row
   const int nb = in_f / 32;
   const int ngrp = in_f / kStepCols;  // in_f % 256 == 0 on this path
-  const int nmine = (ngrp + KS - 1) / KS;
-  const int sbeg = part * nmine;
-  const int send = sbeg + nmine < ngrp ? sbeg + nmine : ngrp;
+  const int nmine = (ngrp + KS - 1) / KS;  // steps part, part + KS, part + 2 KS, ..
 
   // Weights: the wave's rows [r0, r0 + nrw) form one resource over their blocks.
   const int nrw = out_f - r0 < kRowsPerWave ? out_f - r0 : kRowsPerWave;
@@ -144,7 +149,7 @@ void k_gemv_q8_0_mfma(const uint8_t *__restrict__ W, int64_t row_bytes,
     float sc;
   };
   auto load_step = [&](Step &st, int s) {
-    const bool in = s < send;  // past this wave's share: past every resource
+    const bool in = s < ngrp;  // past the row: past every resource
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
       st.w[q] = buf_load16_stream(wrs, in && woff[q] != kPastEnd ? woff[q] + (uint32_t)(kGrpBytes * s) : kPastEnd);
@@ -153,16 +158,16 @@ void k_gemv_q8_0_mfma(const uint8_t *__restrict__ W, int64_t row_bytes,
     st.sc = buf_load_f32(drs, in ? (doff + (uint32_t)(kGrpBlocks * s)) * 4 : kPastEnd);
   };
   Step st;
-  load_step(st, sbeg);
+  load_step(st, part);
 
   const int fi = lane % 16, fg = lane / 16;  // fragment row (A) / column (B), k-group
-  const unsigned char *arow = rl + fi * kAPitch + 2 + 8 * fg;
+  const unsigned char *arow = rl + fi * kAPitch + 8 * fg;  // 8-byte aligned
   const unsigned char *brow = rb + (fi % kMT) * kBPitch + 8 * fg;
   const float *drow = rd + (fi % kMT) * kGrpBlocks;
   float4_t acc[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) acc[a] = float4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = sbeg; s < sbeg + nmine; ++s) {
+  for (int s = part; s < part + KS * nmine; s += KS) {
     wave_lds_fence();
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
@@ -177,12 +182,23 @@ void k_gemv_q8_0_mfma(const uint8_t *__restrict__ W, int64_t row_bytes,
     for (int h = 0; h < 2; ++h)
       *reinterpret_cast<int4_t *>(rb + arw * kBPitch + 32 * apc + 16 * h) = st.a[h];
     rd[arw * kGrpBlocks + apc] = st.sc;
-    load_step(st, s + 1);
+    load_step(st, s + KS);
     wave_lds_fence();
 #pragma unroll
     for (int k = 0; k < kGrpBlocks; ++k) {
+      // Block k's quants start at byte 34k + 2 of the row: 4-byte aligned for odd k, 2 bytes
+      // past a dword for even k.  Odd k: two aligned dwords.  Even k: three aligned dwords
+      // funnel-shifted by 2 bytes (an unaligned LDS read costs more than the extra dword).
       long wa, xb;
-      __builtin_memcpy(&wa, arow + 34 * k, 8);  // 2-byte aligned
+      if (k % 2) {
+        const uint32_t *a4 = reinterpret_cast<const uint32_t *>(arow + 34 * k + 2);
+        wa = (long)((uint64_t)a4[0] | ((uint64_t)a4[1] << 32));
+      } else {
+        const uint32_t *a4 = reinterpret_cast<const uint32_t *>(arow + 34 * k);
+        const uint32_t d0 = a4[0], d1 = a4[1], d2 = a4[2];
+        wa = (long)((uint64_t)__builtin_amdgcn_alignbyte(d1, d0, 2) |
+                    ((uint64_t)__builtin_amdgcn_alignbyte(d2, d1, 2) << 32));
+      }
       __builtin_memcpy(&xb, brow + 32 * k, 8);
       const float4_t dw = *reinterpret_cast<const float4_t *>(rw + k * kRowsPerWave + 4 * fg);
       const float da = drow[k];
