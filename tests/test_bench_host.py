@@ -138,3 +138,41 @@ def test_summarize_sq_derives_shares_from_counters_and_duration(tmp_path):
     cells = [c.strip() for c in line.strip("|").split("|")]
     assert cells[1:] == ["10.00", "50.00", "10.00", "25.00", "2.00", "30.00", "3072.00",
                          "20.00", "0.10"]
+
+
+def test_summarize_mem_request_ratios(tmp_path):
+    # One e4m3 17408x5120 launch (87,040 KiB of weights) over two counter passes, and one
+    # Q8_0-row read kernel: per-KiB counts, L1->L2 requests per memory request, hit rate and
+    # mean latency.
+    fam, cfg, grid, wg, _ = bench.launch_signature("e4m3", 17408, 5120)
+    gemv = f"void fp8gemv::(anonymous namespace)::{fam}, fp8gemv::{cfg} >(int)"
+    read = "void fp8gemv::(anonymous namespace)::k_read_rows<51>(int)"
+    kib = 17408 * 5120 / 1024
+    passes = [
+        {"TCC_REQ_sum": 9 * kib, "TCC_EA0_RDREQ_sum": 8 * kib, "TCC_EA0_RDREQ_32B_sum": 0,
+         "TCC_HIT_sum": kib},
+        {"TCC_MISS_sum": 9 * kib, "TCP_TCC_READ_REQ_sum": 10 * kib,
+         "TCP_TCC_READ_REQ_LATENCY_sum": 10 * kib * 800},
+    ]
+    paths = []
+    for i, counters in enumerate(passes):
+        rows = []
+        for name, g, dram in ((gemv, grid, None), (read, 1114112, 1000.0)):
+            for c, v in counters.items():
+                if dram is not None:  # the read kernel: 1000 memory requests, 1130 L1->L2
+                    v = {"TCC_EA0_RDREQ_sum": dram, "TCP_TCC_READ_REQ_sum": 1130.0}.get(c, 1.0)
+                rows.append({"Dispatch_Id": str(i), "Kernel_Name": name, "Grid_Size": str(g),
+                             "Workgroup_Size": str(wg), "LDS_Block_Size": "0",
+                             "Counter_Name": c, "Counter_Value": str(v)})
+        p = tmp_path / f"pass{i}.csv"
+        _write_csv(p, rows)
+        paths.append(str(p))
+    out = bench.summarize_mem(paths)
+    line = [l for l in out.splitlines() if l.startswith("| e4m3@17408x5120 |")][0]
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    dram_mb = 8 * kib * 128 / 1e6
+    assert cells[2:] == [f"{dram_mb:.2f}", "1.25", "9.00", "8.00", "0.00", "10.00", "10.00",
+                         "800.00"]
+    read_line = [l for l in out.splitlines() if l.startswith("| read |") and "k_read_rows<51>" in l][0]
+    cells = [c.strip() for c in read_line.strip("|").split("|")]
+    assert cells[2:4] == ["0.13", "1.13"] and cells[4] == "-"  # no per-KiB figures for reads
