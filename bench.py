@@ -135,21 +135,24 @@ class Arm:
         self.y = torch.empty(MAX_M * out_f, device=dev)
         self.i = 0
 
-    def launch(self, qs, d, m=1):
+    def launch(self, qs, d, m=1, mc=False):
         c = self.i % self.copies
         self.i += 1
-        self.launch_copy(qs, d, c, m)
+        self.launch_copy(qs, d, c, m, mc)
 
-    def launch_copy(self, qs, d, c, m=1):
-        fg = self.fg
+    def launch_copy(self, qs, d, c, m=1, mc=False):
+        """The container's GEMV on copy c; mc: its matrix-core entry point (*_mc)."""
+        fg, sfx = self.fg, "_mc" if mc else ""
         if self.arm == "q8_0":
-            fg.gemv_q8_0_q81(self.W[c], self.row_bytes, qs, d, self.y, m, self.in_f, self.out_f)
+            getattr(fg, "gemv_q8_0_q81" + sfx)(self.W[c], self.row_bytes, qs, d, self.y, m,
+                                               self.in_f, self.out_f)
         elif self.arm == "e4m3":
-            fg.gemv_e4m3_q81(self.W[c], self.row_bytes, SCALE, qs, d, self.y, m, self.in_f,
-                             self.out_f)
+            getattr(fg, "gemv_e4m3_q81" + sfx)(self.W[c], self.row_bytes, SCALE, qs, d, self.y, m,
+                                               self.in_f, self.out_f)
         else:
-            fg.gemv_e4m3_blk128_q81(self.W[c], self.row_bytes, self.grids[c], self.grid_cols, qs,
-                                    d, self.y, m, self.in_f, self.out_f)
+            getattr(fg, "gemv_e4m3_blk128_q81" + sfx)(self.W[c], self.row_bytes, self.grids[c],
+                                                      self.grid_cols, qs, d, self.y, m,
+                                                      self.in_f, self.out_f)
 
 
 def cpu_model() -> str:
@@ -643,10 +646,11 @@ def main() -> int:
         gaps = sorted(evs[i][1].elapsed_time(evs[i + 1][0]) * 1e3 for i in range(n - 1))
         return t, gaps[len(gaps) // 2]
 
-    def run_m_rows():
+    def run_m_rows(mc=False):
         """Small-batch rows (gemv_e4m3_bench.rs: m in {1, 2, 4, 8} through grid.y at
         17408x5120): m activation rows from the producer with nrows = m, one GEMV call per
-        launch, weights counted once per call."""
+        launch, weights counted once per call.  mc: the matrix-core entry points instead of
+        the plain ones (whose rows are bit-identical to m = 1)."""
         out = {}
         out_f, in_f = SHAPE_M
         xm = torch.from_numpy(synth.x_rows(in_f, MAX_M)).to(dev)
@@ -658,7 +662,7 @@ def main() -> int:
             obj = arm_objs[(out_f, in_f, a)]
             for m in M_ROWS:
                 n = max(args.kernel_iters, obj.copies)
-                g = capture(lambda: [obj.launch(qsm, dm, m) for _ in range(n)])
+                g = capture(lambda: [obj.launch(qsm, dm, m, mc) for _ in range(n)])
                 g.replay()
                 us = timed(g.replay, n) * 1e3
                 wb = weight_bytes(a, out_f, in_f)
@@ -666,7 +670,8 @@ def main() -> int:
                     "us": round(us, 3), "us_per_row": round(us / m, 3),
                     "weight_GBs": round(wb / us / 1e3, 1),
                     "alg_bytes": algorithmic_bytes(a, out_f, in_f, m)}
-                log(f"{a:7s} {out_f}x{in_f} m={m}: {us:8.2f} us  {us / m:7.2f} us/row")
+                log(f"{a:7s} {out_f}x{in_f} m={m}{' matrix cores' if mc else ''}: {us:8.2f} us  "
+                    f"{us / m:7.2f} us/row")
         return out
 
     if args.m_rows_only:
@@ -675,7 +680,8 @@ def main() -> int:
         if SHAPE_M not in shapes:
             log(f"--m-rows-only needs --shapes to include {SHAPE_M[0]}x{SHAPE_M[1]}")
             return 2
-        print(json.dumps({"m_rows": run_m_rows()}), flush=True)
+        print(json.dumps({"m_rows": run_m_rows(),
+                          "m_rows_matrix_cores": run_m_rows(mc=True)}), flush=True)
         return 0
 
     if args.copy_mib:
@@ -749,6 +755,7 @@ def main() -> int:
                                     **detail[f"{a}@{out_f}x{in_f}"]}) + "\n")
 
     m_rows = run_m_rows() if SHAPE_M in shapes and not args.kernels_only else {}
+    m_rows_mc = run_m_rows(mc=True) if SHAPE_M in shapes and not args.kernels_only else {}
 
     # Projection shape sheets (gemv_e4m3_bench.rs, main: the 27B and 1.7B sheets, the three
     # arms per shape on their own rotated copies, ratio = t_q8_0 / t_e4m3, ratio_blk =
@@ -1076,7 +1083,7 @@ def main() -> int:
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
         "gemv": detail, "read_ceiling": ceiling, "read_fit": read_fit,
         "read_patterns": read_patterns, "q8_0_read_ceiling": q8_ceiling, "fixed_cost": fixed,
-        "m_rows": m_rows, "sheets": sheets,
+        "m_rows": m_rows, "m_rows_matrix_cores": m_rows_mc, "sheets": sheets,
         "requant": requant,
         "producer_us": prod_us,
         "roofline": roofline, "cpu_baseline": cpu, "cold_check": cold,

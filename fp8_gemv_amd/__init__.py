@@ -33,7 +33,8 @@ FP8GEMV_MAX_M = 65535
 EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "silu_mul_f32", "silu_mul_q8_1",
            "gated_rms_norm_f32", "gated_rmsnorm_q8_1",
            "gemv_q8_0_q81", "gemv_e4m3_q81",
-           "gemv_e4m3_blk128_q81", "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
+           "gemv_e4m3_blk128_q81", "gemv_q8_0_q81_mc", "gemv_e4m3_q81_mc",
+           "gemv_e4m3_blk128_q81_mc", "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
            "fp8gemv_read_bytes", "fp8gemv_read_pattern", "fp8gemv_gemv_launch_info",
            "fp8gemv_strerror")
 
@@ -41,7 +42,12 @@ EXPORTS = ("rms_norm_f32", "quantize_q8_1", "rmsnorm_q8_1", "silu_mul_f32", "sil
 FP8GEMV_Q8_0 = 0
 FP8GEMV_E4M3 = 1
 FP8GEMV_E4M3_BLK128 = 2
-CONTAINERS = {"q8_0": FP8GEMV_Q8_0, "e4m3": FP8GEMV_E4M3, "blk128": FP8GEMV_E4M3_BLK128}
+FP8GEMV_Q8_0_MC = 3
+FP8GEMV_E4M3_MC = 4
+FP8GEMV_E4M3_BLK128_MC = 5
+CONTAINERS = {"q8_0": FP8GEMV_Q8_0, "e4m3": FP8GEMV_E4M3, "blk128": FP8GEMV_E4M3_BLK128,
+              "q8_0_mc": FP8GEMV_Q8_0_MC, "e4m3_mc": FP8GEMV_E4M3_MC,
+              "blk128_mc": FP8GEMV_E4M3_BLK128_MC}
 
 
 class LaunchInfo(ctypes.Structure):
@@ -77,6 +83,9 @@ def _load() -> ctypes.CDLL:
         "gemv_q8_0_q81": [vp, i64, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_q81": [vp, i64, f32, vp, vp, vp, i32, i32, i32, vp],
         "gemv_e4m3_blk128_q81": [vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, vp],
+        "gemv_q8_0_q81_mc": [vp, i64, vp, vp, vp, i32, i32, i32, vp],
+        "gemv_e4m3_q81_mc": [vp, i64, f32, vp, vp, vp, i32, i32, i32, vp],
+        "gemv_e4m3_blk128_q81_mc": [vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, vp],
         "requant_e4m3_q8_0": [vp, i64, f32, vp, i64, i32, i32, vp],
         "requant_e4m3_blk128_q8_0": [vp, i64, vp, i32, vp, i64, i32, i32, vp],
     }
@@ -251,10 +260,10 @@ def _w_numel(row_bytes: int, out_f: int, container_row: int) -> int:
 
 
 def gemv_q8_0_q81(W, row_bytes: int, qs, d, y, m: int, in_f: int, out_f: int,
-                  stream=None) -> None:
+                  stream=None, _entry="gemv_q8_0_q81") -> None:
     """y[m, out_f] = Q8_0 weight rows W times the q8_1 activation (qs, d)."""
     dev = _dev(W)
-    _run("gemv_q8_0_q81", dev,
+    _run(_entry, dev,
          _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f // 32 * 34), dev), row_bytes,
          _ptr(qs, "qs", torch.int8, m * in_f, dev),
          _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
@@ -263,10 +272,10 @@ def gemv_q8_0_q81(W, row_bytes: int, qs, d, y, m: int, in_f: int, out_f: int,
 
 
 def gemv_e4m3_q81(W, row_bytes: int, scale: float, qs, d, y, m: int, in_f: int, out_f: int,
-                  stream=None) -> None:
+                  stream=None, _entry="gemv_e4m3_q81") -> None:
     """y[m, out_f] = scale * e4m3 weights W times the q8_1 activation (qs, d)."""
     dev = _dev(W)
-    _run("gemv_e4m3_q81", dev,
+    _run(_entry, dev,
          _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f), dev), row_bytes, scale,
          _ptr(qs, "qs", torch.int8, m * in_f, dev),
          _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
@@ -275,16 +284,37 @@ def gemv_e4m3_q81(W, row_bytes: int, scale: float, qs, d, y, m: int, in_f: int, 
 
 
 def gemv_e4m3_blk128_q81(W, row_bytes: int, grid, grid_cols: int, qs, d, y, m: int, in_f: int,
-                         out_f: int, stream=None) -> None:
+                         out_f: int, stream=None, _entry="gemv_e4m3_blk128_q81") -> None:
     """y[m, out_f] = block-128-scaled e4m3 weights W times the q8_1 activation (qs, d)."""
     dev = _dev(W)
-    _run("gemv_e4m3_blk128_q81", dev,
+    _run(_entry, dev,
          _ptr(W, "W", torch.uint8, _w_numel(row_bytes, out_f, in_f), dev), row_bytes,
          _ptr(grid, "grid", torch.float32, ((out_f + 127) // 128) * grid_cols, dev), grid_cols,
          _ptr(qs, "qs", torch.int8, m * in_f, dev),
          _ptr(d, "d", torch.float32, m * (in_f // 32), dev),
          _ptr(y, "y", torch.float32, m * out_f, dev),
          m, in_f, out_f, _stream(stream, dev))
+
+
+def gemv_q8_0_q81_mc(W, row_bytes: int, qs, d, y, m: int, in_f: int, out_f: int,
+                     stream=None) -> None:
+    """gemv_q8_0_q81 on the matrix cores (rows agree with it to rounding, not bit for bit)."""
+    gemv_q8_0_q81(W, row_bytes, qs, d, y, m, in_f, out_f, stream, _entry="gemv_q8_0_q81_mc")
+
+
+def gemv_e4m3_q81_mc(W, row_bytes: int, scale: float, qs, d, y, m: int, in_f: int, out_f: int,
+                     stream=None) -> None:
+    """gemv_e4m3_q81 on the matrix cores (rows agree with it to rounding, not bit for bit)."""
+    gemv_e4m3_q81(W, row_bytes, scale, qs, d, y, m, in_f, out_f, stream,
+                  _entry="gemv_e4m3_q81_mc")
+
+
+def gemv_e4m3_blk128_q81_mc(W, row_bytes: int, grid, grid_cols: int, qs, d, y, m: int,
+                            in_f: int, out_f: int, stream=None) -> None:
+    """gemv_e4m3_blk128_q81 on the matrix cores (rows agree with it to rounding, not bit for
+    bit)."""
+    gemv_e4m3_blk128_q81(W, row_bytes, grid, grid_cols, qs, d, y, m, in_f, out_f, stream,
+                         _entry="gemv_e4m3_blk128_q81_mc")
 
 
 # --------------------------------------------------------------------------- requantiser

@@ -107,29 +107,32 @@ int gated_rmsnorm_q8_1(const float *o, const float *g, const float *w, float *z,
                                                       eps, (hipStream_t)stream));
 }
 
-int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
-                  int m, int in_f, int out_f, void *stream) {
+namespace {
+int gemv_q8_0_call(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
+                   int m, int in_f, int out_f, bool matrix_cores, void *stream) {
   const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);
   if (rc) return rc;
   if (row_bytes < (int64_t)(in_f / 32) * 34) return FP8GEMV_ERR_ROW_BYTES;
   if (!aligned(W, 2) || row_bytes % 2 != 0) return FP8GEMV_ERR_ALIGN;
   return launch_rc(fp8gemv::launch_gemv_q8_0(static_cast<const uint8_t *>(W), row_bytes, qs, d,
-                                             y, m, in_f, out_f, (hipStream_t)stream));
+                                             y, m, in_f, out_f, matrix_cores,
+                                             (hipStream_t)stream));
 }
 
-int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
-                  const float *d, float *y, int m, int in_f, int out_f, void *stream) {
+int gemv_e4m3_call(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
+                   const float *d, float *y, int m, int in_f, int out_f, bool matrix_cores,
+                   void *stream) {
   const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);
   if (rc) return rc;
   if (row_bytes < in_f) return FP8GEMV_ERR_ROW_BYTES;
   if (!aligned(W, 16) || row_bytes % 16 != 0) return FP8GEMV_ERR_ALIGN;
   return launch_rc(fp8gemv::launch_gemv_e4m3(W, row_bytes, scale, nullptr, 0, false, qs, d, y, m,
-                                             in_f, out_f, (hipStream_t)stream));
+                                             in_f, out_f, matrix_cores, (hipStream_t)stream));
 }
 
-int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid, int grid_cols,
-                         const int8_t *qs, const float *d, float *y, int m, int in_f, int out_f,
-                         void *stream) {
+int gemv_e4m3_blk128_call(const uint8_t *W, int64_t row_bytes, const float *grid, int grid_cols,
+                          const int8_t *qs, const float *d, float *y, int m, int in_f,
+                          int out_f, bool matrix_cores, void *stream) {
   const int rc = check_gemv_common(W, qs, d, y, m, in_f, out_f);
   if (rc) return rc;
   if (!grid) return FP8GEMV_ERR_NULL;
@@ -137,7 +140,42 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
   if (row_bytes < in_f) return FP8GEMV_ERR_ROW_BYTES;
   if (!aligned(W, 16) || row_bytes % 16 != 0 || !aligned(grid, 4)) return FP8GEMV_ERR_ALIGN;
   return launch_rc(fp8gemv::launch_gemv_e4m3(W, row_bytes, 1.0f, grid, grid_cols, true, qs, d, y,
-                                             m, in_f, out_f, (hipStream_t)stream));
+                                             m, in_f, out_f, matrix_cores, (hipStream_t)stream));
+}
+}  // namespace
+
+int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
+                  int m, int in_f, int out_f, void *stream) {
+  return gemv_q8_0_call(W, row_bytes, qs, d, y, m, in_f, out_f, false, stream);
+}
+
+int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
+                  const float *d, float *y, int m, int in_f, int out_f, void *stream) {
+  return gemv_e4m3_call(W, row_bytes, scale, qs, d, y, m, in_f, out_f, false, stream);
+}
+
+int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid, int grid_cols,
+                         const int8_t *qs, const float *d, float *y, int m, int in_f, int out_f,
+                         void *stream) {
+  return gemv_e4m3_blk128_call(W, row_bytes, grid, grid_cols, qs, d, y, m, in_f, out_f, false,
+                               stream);
+}
+
+int gemv_q8_0_q81_mc(const void *W, int64_t row_bytes, const int8_t *qs, const float *d,
+                     float *y, int m, int in_f, int out_f, void *stream) {
+  return gemv_q8_0_call(W, row_bytes, qs, d, y, m, in_f, out_f, true, stream);
+}
+
+int gemv_e4m3_q81_mc(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
+                     const float *d, float *y, int m, int in_f, int out_f, void *stream) {
+  return gemv_e4m3_call(W, row_bytes, scale, qs, d, y, m, in_f, out_f, true, stream);
+}
+
+int gemv_e4m3_blk128_q81_mc(const uint8_t *W, int64_t row_bytes, const float *grid,
+                            int grid_cols, const int8_t *qs, const float *d, float *y, int m,
+                            int in_f, int out_f, void *stream) {
+  return gemv_e4m3_blk128_call(W, row_bytes, grid, grid_cols, qs, d, y, m, in_f, out_f, true,
+                               stream);
 }
 
 namespace {
@@ -202,14 +240,20 @@ int fp8gemv_gemv_launch_info(int container, const void *W, int64_t row_bytes, in
   if (m < 1 || out_f < 1 || bad_cols(in_f)) return FP8GEMV_ERR_SHAPE;
   if (in_f > FP8GEMV_MAX_IN_F || m > FP8GEMV_MAX_M) return FP8GEMV_ERR_TOO_LARGE;
   fp8gemv::LaunchDesc r;
-  if (container == FP8GEMV_Q8_0) {
+  const bool mc = container == FP8GEMV_Q8_0_MC || container == FP8GEMV_E4M3_MC ||
+                  container == FP8GEMV_E4M3_BLK128_MC;
+  if (container == FP8GEMV_Q8_0 || container == FP8GEMV_Q8_0_MC) {
     if (row_bytes < (int64_t)(in_f / 32) * 34) return FP8GEMV_ERR_ROW_BYTES;
     if (!aligned(W, 2) || row_bytes % 2 != 0) return FP8GEMV_ERR_ALIGN;
-    r = fp8gemv::describe_gemv_q8_0(static_cast<const uint8_t *>(W), row_bytes, m, in_f, out_f);
-  } else if (container == FP8GEMV_E4M3 || container == FP8GEMV_E4M3_BLK128) {
+    r = fp8gemv::describe_gemv_q8_0(static_cast<const uint8_t *>(W), row_bytes, m, in_f, out_f,
+                                    mc);
+  } else if (container == FP8GEMV_E4M3 || container == FP8GEMV_E4M3_BLK128 ||
+             container == FP8GEMV_E4M3_MC || container == FP8GEMV_E4M3_BLK128_MC) {
     if (row_bytes < in_f) return FP8GEMV_ERR_ROW_BYTES;
     if (!aligned(W, 16) || row_bytes % 16 != 0) return FP8GEMV_ERR_ALIGN;
-    r = fp8gemv::describe_gemv_e4m3(container == FP8GEMV_E4M3_BLK128, row_bytes, m, in_f, out_f);
+    r = fp8gemv::describe_gemv_e4m3(
+        container == FP8GEMV_E4M3_BLK128 || container == FP8GEMV_E4M3_BLK128_MC, row_bytes, m,
+        in_f, out_f, mc);
   } else {
     return FP8GEMV_ERR_SHAPE;
   }

@@ -144,28 +144,35 @@ hipError_t launch_gated_rmsnorm_q8_1(const float *o, const float *g, const float
                                      float eps, hipStream_t s);
 hipError_t launch_silu_mul_q8_1(const float *g, const float *u, float *h, int8_t *qs, float *d,
                                 int ncols, int nrows, hipStream_t s);
+// matrix_cores: run the matrix-core kernel where the row layout allows it (the *_mc entry
+// points); otherwise, and always for the plain entry points, the vector kernels, whose rows are
+// bit-identical to m = 1 for any m.
 hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                             int grid_cols, bool blk128, const int8_t *qs, const float *d,
-                            float *y, int m, int in_f, int out_f, hipStream_t s);
+                            float *y, int m, int in_f, int out_f, bool matrix_cores,
+                            hipStream_t s);
 hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
-                            const float *d, float *y, int m, int in_f, int out_f, hipStream_t s);
-LaunchDesc describe_gemv_e4m3(bool blk128, int64_t row_bytes, int m, int in_f, int out_f);
-// The matrix-core kernel for several activation rows (gemv_e4m3_mfma.hip); launch_gemv_e4m3
-// and describe_gemv_e4m3 choose it where gemv_e4m3_mfma_applies.
-bool gemv_e4m3_mfma_applies(int64_t row_bytes, int m, int in_f);
+                            const float *d, float *y, int m, int in_f, int out_f,
+                            bool matrix_cores, hipStream_t s);
+LaunchDesc describe_gemv_e4m3(bool blk128, int64_t row_bytes, int m, int in_f, int out_f,
+                              bool matrix_cores);
+// The matrix-core kernel for several activation rows (gemv_e4m3_mfma.hip): the row layouts it
+// takes.
+bool gemv_e4m3_mfma_applies(int64_t row_bytes, int in_f);
 hipError_t launch_gemv_e4m3_mfma(const uint8_t *W, int64_t row_bytes, float scale,
                                  const float *grid, int grid_cols, bool blk128, const int8_t *qs,
                                  const float *d, float *y, int m, int in_f, int out_f,
                                  hipStream_t s);
 LaunchDesc describe_gemv_e4m3_mfma(bool blk128, int m, int in_f, int out_f);
-// The matrix-core kernel for several activation rows over Q8_0 (gemv_q8_0_mfma.hip);
-// launch_gemv_q8_0 and describe_gemv_q8_0 choose it where gemv_q8_0_mfma_applies.
-bool gemv_q8_0_mfma_applies(const uint8_t *W, int64_t row_bytes, int m, int in_f);
+// The matrix-core kernel for several activation rows over Q8_0 (gemv_q8_0_mfma.hip): the row
+// layouts it takes.
+bool gemv_q8_0_mfma_applies(const uint8_t *W, int64_t row_bytes, int in_f);
 hipError_t launch_gemv_q8_0_mfma(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
                                  const float *d, float *y, int m, int in_f, int out_f,
                                  hipStream_t s);
 LaunchDesc describe_gemv_q8_0_mfma(int m, int in_f, int out_f);
-LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f);
+LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f,
+                              bool matrix_cores);
 hipError_t launch_requant_q8_0(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                                int grid_cols, bool blk128, void *Wq, int64_t q_row_bytes,
                                int in_f, int out_f, hipStream_t s);

@@ -388,16 +388,19 @@ hipError_t dispatch(const uint8_t *W, int64_t row_bytes, float scale, const floa
 
 hipError_t launch_gemv_e4m3(const uint8_t *W, int64_t row_bytes, float scale, const float *grid,
                             int grid_cols, bool blk128, const int8_t *qs, const float *d,
-                            float *y, int m, int in_f, int out_f, hipStream_t s) {
-  if (gemv_e4m3_mfma_applies(row_bytes, m, in_f))
+                            float *y, int m, int in_f, int out_f, bool matrix_cores,
+                            hipStream_t s) {
+  if (matrix_cores && gemv_e4m3_mfma_applies(row_bytes, in_f))
     return launch_gemv_e4m3_mfma(W, row_bytes, scale, grid, grid_cols, blk128, qs, d, y, m, in_f,
                                  out_f, s);
   if (blk128) return dispatch<true>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
   return dispatch<false>(W, row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f, s);
 }
 
-LaunchDesc describe_gemv_e4m3(bool blk128, int64_t row_bytes, int m, int in_f, int out_f) {
-  if (gemv_e4m3_mfma_applies(row_bytes, m, in_f)) return describe_gemv_e4m3_mfma(blk128, m, in_f, out_f);
+LaunchDesc describe_gemv_e4m3(bool blk128, int64_t row_bytes, int m, int in_f, int out_f,
+                              bool matrix_cores) {
+  if (matrix_cores && gemv_e4m3_mfma_applies(row_bytes, in_f))
+    return describe_gemv_e4m3_mfma(blk128, m, in_f, out_f);
   return with_cfg(m, in_f, [&](auto tag) {
     using C = typename decltype(tag)::type;
     LaunchDesc r;

@@ -292,10 +292,10 @@ auto with_mcfg(int in_f, F &&f) {
 
 }  // namespace
 
-bool gemv_e4m3_mfma_applies(int64_t row_bytes, int m, int in_f) {
+bool gemv_e4m3_mfma_applies(int64_t row_bytes, int in_f) {
   (void)in_f;
   // offsets of the wave's 16 rows stay below the past-the-end offset
-  return m >= 3 && row_bytes <= ((int64_t)1 << 26);
+  return row_bytes <= ((int64_t)1 << 26);
 }
 
 hipError_t launch_gemv_e4m3_mfma(const uint8_t *W, int64_t row_bytes, float scale,

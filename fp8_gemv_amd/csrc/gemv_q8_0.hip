@@ -490,8 +490,9 @@ bool fast_path(const uint8_t *W, int64_t row_bytes, int in_f) {
 }  // namespace
 
 hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *qs,
-                            const float *d, float *y, int m, int in_f, int out_f, hipStream_t s) {
-  if (gemv_q8_0_mfma_applies(W, row_bytes, m, in_f))
+                            const float *d, float *y, int m, int in_f, int out_f,
+                            bool matrix_cores, hipStream_t s) {
+  if (matrix_cores && gemv_q8_0_mfma_applies(W, row_bytes, in_f))
     return launch_gemv_q8_0_mfma(W, row_bytes, qs, d, y, m, in_f, out_f, s);
   if (fast_path(W, row_bytes, in_f)) {
     return with_cfg(m, in_f, [&](auto tag) {
@@ -505,8 +506,10 @@ hipError_t launch_gemv_q8_0(const uint8_t *W, int64_t row_bytes, const int8_t *q
   return hipGetLastError();
 }
 
-LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f) {
-  if (gemv_q8_0_mfma_applies(W, row_bytes, m, in_f)) return describe_gemv_q8_0_mfma(m, in_f, out_f);
+LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in_f, int out_f,
+                              bool matrix_cores) {
+  if (matrix_cores && gemv_q8_0_mfma_applies(W, row_bytes, in_f))
+    return describe_gemv_q8_0_mfma(m, in_f, out_f);
   if (fast_path(W, row_bytes, in_f)) {
     return with_cfg(m, in_f, [&](auto tag) {
       using C = typename decltype(tag)::type;

@@ -246,10 +246,10 @@ auto with_qmcfg(int in_f, F &&f) {
 
 }  // namespace
 
-bool gemv_q8_0_mfma_applies(const uint8_t *W, int64_t row_bytes, int m, int in_f) {
+bool gemv_q8_0_mfma_applies(const uint8_t *W, int64_t row_bytes, int in_f) {
   // whole groups, 16-byte aligned rows (the chunk loads), and offsets of the wave's 16 rows
   // below the past-the-end offset
-  return m >= 3 && in_f % 256 == 0 && row_bytes % 16 == 0 &&
+  return in_f % 256 == 0 && row_bytes % 16 == 0 &&
          (reinterpret_cast<uintptr_t>(W) & 15) == 0 && row_bytes <= ((int64_t)1 << 26);
 }
 

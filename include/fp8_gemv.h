@@ -158,11 +158,9 @@ int gated_rmsnorm_q8_1(const float *o, const float *g, const float *w, float *z,
  * Alignment: W and row_bytes 2-byte aligned; the fast path also needs W 16-byte aligned,
  * row_bytes % 16 == 0 and in_f % 256 == 0, otherwise a slower path runs.  qs, d 16-byte
  * aligned.  Each activation row is computed independently.  Every block's integer sum is
- * exact.  For m <= 2, off the fast path, or with a row_bytes of 64 MiB or more, row t of an
- * m-row call is bit-identical to an m=1 call on that row.  For m >= 3 on the fast path the
- * products run on the matrix cores and the scaling follows a different (fixed) order: row t
- * is then bit-identical to the same row in any other such call, whatever its position and
- * the other rows, and agrees with m=1 to rounding.
+ * exact.  Up to 8 activation rows share one pass over the weights, and row t of an m-row
+ * call is bit-identical to an m=1 call on that row, for every m (the batched arms' bit-parity
+ * gate, gemv_e4m3_bench.rs, WHAT MADE THIS A BOUNDED WRITE).
  */
 int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const float *d, float *y,
                   int m, int in_f, int out_f, void *stream);
@@ -176,11 +174,8 @@ int gemv_q8_0_q81(const void *W, int64_t row_bytes, const int8_t *qs, const floa
  *   row_bytes  >= in_f, multiple of 16;  W 16-byte aligned
  *   scale      per-tensor dequantisation factor, applied once per output
  *   qs, d, y   as for gemv_q8_0_q81
- * Each activation row is computed independently.  For m <= 2 (or a row_bytes of 64 MiB or
- * more) row t of an m-row call is bit-identical to an m=1 call on that row.  For m >= 3 the
- * products run on the matrix cores with a different (fixed) summation order: row t is then
- * bit-identical to the same row in any other call with m >= 3, whatever its position and the
- * other rows, and agrees with m=1 to rounding.
+ * Each activation row is computed independently; up to 8 share one pass over the weights,
+ * and row t of an m-row call is bit-identical to an m=1 call on that row, for every m.
  */
 int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
                   const float *d, float *y, int m, int in_f, int out_f, void *stream);
@@ -199,6 +194,31 @@ int gemv_e4m3_q81(const uint8_t *W, int64_t row_bytes, float scale, const int8_t
 int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid, int grid_cols,
                          const int8_t *qs, const float *d, float *y, int m, int in_f, int out_f,
                          void *stream);
+
+/*
+ * gemv_q8_0_q81_mc, gemv_e4m3_q81_mc, gemv_e4m3_blk128_q81_mc -- the same three products, with
+ * the same arguments, checks and return codes, for several activation rows on the matrix
+ * cores (v_mfma_i32_16x16x32_i8 for Q8_0, v_mfma_f32_16x16x32_f16 for e4m3): 16 weight rows x
+ * up to 8 activation rows per instruction, one q8_1 block (K = 32) at a time.  Opt-in: at
+ * m >= 3 the vector kernels of the plain entry points are bound by their per-row arithmetic,
+ * not by the weight stream, and these keep the cost nearly flat in m (17408 x 5120: m = 8
+ * takes 1.4-1.5x m = 1, against 3x on the vector kernels).
+ * What they give up is the bit-parity gate of the batched arms: each block's sum is formed by
+ * the matrix core and the block sums are added in a fixed order of their own, so a row agrees
+ * with the plain entry point to rounding (within the parity tolerance, 1e-5 of the sum of the
+ * terms' magnitudes), not bit for bit.  A row is bit-identical to the same row in any other
+ * call of the same entry point, whatever m, its position and the other rows.
+ * Row layouts the matrix-core kernels do not take run the plain entry point's kernels: a
+ * row_bytes above 64 MiB, and for Q8_0 anything off its fast path (in_f % 256 != 0, W or
+ * row_bytes not 16-byte aligned).
+ */
+int gemv_q8_0_q81_mc(const void *W, int64_t row_bytes, const int8_t *qs, const float *d,
+                     float *y, int m, int in_f, int out_f, void *stream);
+int gemv_e4m3_q81_mc(const uint8_t *W, int64_t row_bytes, float scale, const int8_t *qs,
+                     const float *d, float *y, int m, int in_f, int out_f, void *stream);
+int gemv_e4m3_blk128_q81_mc(const uint8_t *W, int64_t row_bytes, const float *grid,
+                            int grid_cols, const int8_t *qs, const float *d, float *y, int m,
+                            int in_f, int out_f, void *stream);
 
 /*
  * requant_e4m3_q8_0 -- load-time requantisation of a raw e4m3 weight plane (per-tensor scale)
@@ -305,7 +325,8 @@ int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_
  * fp8gemv_gemv_launch_info -- what one GEMV call with these arguments would launch, without
  * launching it: for profilers and benches that label kernel traces.  The library's own launch
  * selection fills it in, so it always agrees with the launch.
- *   container   FP8GEMV_Q8_0, FP8GEMV_E4M3 or FP8GEMV_E4M3_BLK128
+ *   container   FP8GEMV_Q8_0, FP8GEMV_E4M3 or FP8GEMV_E4M3_BLK128 (the plain entry points), or
+ *               FP8GEMV_Q8_0_MC, FP8GEMV_E4M3_MC or FP8GEMV_E4M3_BLK128_MC (the *_mc ones)
  *   W, row_bytes, m, in_f, out_f   as for that container's GEMV; W is never dereferenced (only
  *               its alignment matters, for the Q8_0 fast-path choice)
  *   info        out: grid in workgroups (x = weight rows, y = activation-row passes), threads per
@@ -317,6 +338,9 @@ int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_
 #define FP8GEMV_Q8_0         0
 #define FP8GEMV_E4M3         1
 #define FP8GEMV_E4M3_BLK128  2
+#define FP8GEMV_Q8_0_MC      3
+#define FP8GEMV_E4M3_MC      4
+#define FP8GEMV_E4M3_BLK128_MC 5
 typedef struct {
   uint32_t grid_x, grid_y;
   uint32_t workgroup_size;

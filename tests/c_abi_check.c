@@ -6,8 +6,9 @@
  *   1. producer (q8_fuse_gate.rs, module doc and `run_shape`): the fused rmsnorm_q8_1 and the
  *      two-launch chain rms_norm_f32 -> quantize_q8_1 give the same z, qs and d bytes, and
  *      the oracle's quantiser applied to the GPU's z gives the GPU's qs and d bit for bit;
- *   2. the three GEMVs (gemv_e4m3_bench.rs, THE COMPARISON and THE BLOCK-128 ARM) on that
- *      q8_1 row: every output within 1e-5 of the sum of the absolute terms of the oracle;
+ *   2. the three GEMVs (gemv_e4m3_bench.rs, THE COMPARISON and THE BLOCK-128 ARM), plain and
+ *      on the matrix cores, on that q8_1 row: every output within 1e-5 of the sum of the
+ *      absolute terms of the oracle;
  *   3. argument errors come back as negative codes with a message, and launch nothing.
  *
  * Inputs come from the shared seeded generators (synth), with the seeds the Python tests use.
@@ -151,14 +152,20 @@ static void run_case(int out_f, int in_f, hipStream_t s) {
   double *y64 = host_alloc(sizeof(double) * out_f), *A = host_alloc(sizeof(double) * out_f);
   const float scale = 0.0625f;
 
-  for (int arm = 0; arm < 3; ++arm) {
-    const char *name = arm == 0 ? "e4m3" : arm == 1 ? "blk128" : "q8_0";
+  /* arms 0..2: the plain entry points; 3..5: the same containers on the matrix cores (*_mc) */
+  for (int k = 0; k < 6; ++k) {
+    const int arm = k % 3, mc = k >= 3;
+    const char *name = k == 0 ? "e4m3" : k == 1 ? "blk128" : k == 2 ? "q8_0"
+                     : k == 3 ? "e4m3_mc" : k == 4 ? "blk128_mc" : "q8_0_mc";
     if (arm == 0) {
-      rc = gemv_e4m3_q81(dWe, in_f, scale, dq1, dd1, dy, 1, in_f, out_f, s);
+      rc = (mc ? gemv_e4m3_q81_mc : gemv_e4m3_q81)(dWe, in_f, scale, dq1, dd1, dy, 1, in_f,
+                                                   out_f, s);
     } else if (arm == 1) {
-      rc = gemv_e4m3_blk128_q81(dWe, in_f, dG, gc, dq1, dd1, dy, 1, in_f, out_f, s);
+      rc = (mc ? gemv_e4m3_blk128_q81_mc : gemv_e4m3_blk128_q81)(dWe, in_f, dG, gc, dq1, dd1,
+                                                                 dy, 1, in_f, out_f, s);
     } else {
-      rc = gemv_q8_0_q81(dWq, (int64_t)qrow, dq1, dd1, dy, 1, in_f, out_f, s);
+      rc = (mc ? gemv_q8_0_q81_mc : gemv_q8_0_q81)(dWq, (int64_t)qrow, dq1, dd1, dy, 1, in_f,
+                                                   out_f, s);
     }
     snprintf(what, sizeof what, "%s %dx%d launches (rc %d: %s)", name, out_f, in_f, rc,
              fp8gemv_strerror(rc));

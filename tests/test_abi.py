@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                                   "silu_mul_f32", "silu_mul_q8_1",
                                   "gated_rms_norm_f32", "gated_rmsnorm_q8_1",
                                   "gemv_q8_0_q81", "gemv_e4m3_q81", "gemv_e4m3_blk128_q81",
-                                  "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
+                                  "gemv_q8_0_q81_mc", "gemv_e4m3_q81_mc",
+                                  "gemv_e4m3_blk128_q81_mc", "requant_e4m3_q8_0", "requant_e4m3_blk128_q8_0",
                                   "fp8gemv_read_bytes", "fp8gemv_read_pattern",
                                   "fp8gemv_gemv_launch_info", "fp8gemv_strerror"])
 
@@ -192,7 +193,8 @@ def test_launch_info_argument_errors_and_agreement(fg):
     ref = ctypes.byref(info)
     assert L.fp8gemv_gemv_launch_info(0, None, 5440, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_NULL
     assert L.fp8gemv_gemv_launch_info(0, FAKE, 5440, 1, 5120, 10, None) == fg.FP8GEMV_ERR_NULL
-    assert L.fp8gemv_gemv_launch_info(3, FAKE, 5440, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_SHAPE
+    for bad in (-1, 6):
+        assert L.fp8gemv_gemv_launch_info(bad, FAKE, 5440, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_SHAPE
     assert L.fp8gemv_gemv_launch_info(0, FAKE, 5440, 0, 5120, 10, ref) == fg.FP8GEMV_ERR_SHAPE
     assert L.fp8gemv_gemv_launch_info(1, FAKE, 5120, 1, 5100, 10, ref) == fg.FP8GEMV_ERR_SHAPE
     assert L.fp8gemv_gemv_launch_info(0, FAKE, 5438, 1, 5120, 10, ref) == fg.FP8GEMV_ERR_ROW_BYTES
@@ -208,6 +210,22 @@ def test_launch_info_argument_errors_and_agreement(fg):
                 assert i["kernel"].startswith("k_gemv_") and "Cfg<" in i["config"]
     g = fg.gemv_launch_info("q8_0", 5440, 1, 5120, 100, w_align=2)
     assert g["kernel"] == "k_gemv_q8_0_generic" and g["config"] == ""
+    # the plain entry points never leave the vector kernels (rows bit-identical to m = 1); the
+    # *_mc ones run the matrix-core kernels for every m where the row layout allows it
+    for c in ("q8_0", "e4m3", "blk128"):
+        rb = 5440 if c == "q8_0" else 5120
+        for m in (1, 2, 3, 4, 8, 9):
+            assert "mfma" not in fg.gemv_launch_info(c, rb, m, 5120, 17408)["kernel"]
+            mc = fg.gemv_launch_info(c + "_mc", rb, m, 5120, 17408)
+            assert mc["kernel"].startswith("k_gemv_" + ("q8_0" if c == "q8_0" else "e4m3") + "_mfma")
+            assert mc["grid_y"] == (m + 7) // 8
+    # layouts the matrix-core kernels do not take fall back to the plain kernels
+    assert fg.gemv_launch_info("q8_0_mc", 5440, 4, 5120, 100, w_align=2)["kernel"] == \
+        "k_gemv_q8_0_generic"
+    assert "mfma" not in fg.gemv_launch_info("q8_0_mc", 96 // 32 * 34 + 14, 4, 96, 100)["kernel"]
+    big = (1 << 26) + 16
+    for c in ("q8_0_mc", "e4m3_mc", "blk128_mc"):
+        assert "mfma" not in fg.gemv_launch_info(c, big, 4, 5120, 100)["kernel"]
 
 
 def test_read_pattern_argument_errors(fg):

@@ -43,20 +43,22 @@ class Case:
         self.Wd = to_dev(self.W)
         self.gd = to_dev(self.grid) if self.grid is not None else None
 
-    def gpu(self, fg, qs=None, d=None, m=None, Wd=None, row_bytes=None):
+    def gpu(self, fg, qs=None, d=None, m=None, Wd=None, row_bytes=None, mc=False):
+        """The plain entry point, or with mc the matrix-core one (*_mc)."""
         m = self.m if m is None else m
+        sfx = "_mc" if mc else ""
         qs = to_dev(self.qs) if qs is None else qs
         d = to_dev(self.d) if d is None else d
         Wd = self.Wd if Wd is None else Wd
         rb = self.row_bytes if row_bytes is None else row_bytes
         y = torch.full((m, self.out_f), float("nan"), device=dev())
         if self.kind == "q8_0":
-            fg.gemv_q8_0_q81(Wd, rb, qs, d, y, m, self.in_f, self.out_f)
+            getattr(fg, "gemv_q8_0_q81" + sfx)(Wd, rb, qs, d, y, m, self.in_f, self.out_f)
         elif self.kind == "e4m3":
-            fg.gemv_e4m3_q81(Wd, rb, SCALE, qs, d, y, m, self.in_f, self.out_f)
+            getattr(fg, "gemv_e4m3_q81" + sfx)(Wd, rb, SCALE, qs, d, y, m, self.in_f, self.out_f)
         else:
-            fg.gemv_e4m3_blk128_q81(Wd, rb, self.gd, self.grid.shape[1], qs, d, y, m,
-                                    self.in_f, self.out_f)
+            getattr(fg, "gemv_e4m3_blk128_q81" + sfx)(Wd, rb, self.gd, self.grid.shape[1], qs, d,
+                                                      y, m, self.in_f, self.out_f)
         return host(y)
 
     def oracle_all(self):
@@ -141,27 +143,19 @@ def test_gemv_sheet_shapes_every_row(fg, kind, out_f, in_f):
     _assert_close(y, yo, A)
 
 
-def on_matrix_cores(kind, m, in_f):
-    """Several activation rows (m >= 3) take the matrix-core kernels: always for the e4m3
-    containers, and for Q8_0 on its fast-path rows (in_f % 256 == 0, aligned rows)."""
-    return m >= 3 and (kind != "q8_0" or in_f % 256 == 0)
-
-
-def row_reference(fg, c, t, m):
-    """Row t of activation rows qs/d computed alone: an m = 1 call, or, where an m-row call
-    runs on the matrix cores, a 5-row call holding row t first and four other rows after it
-    (so row t sits at another position among other rows)."""
-    if not on_matrix_cores(c.kind, m, c.in_f):
+def row_reference(fg, c, t, mc=False):
+    """Row t of activation rows qs/d computed alone.  Plain entry point: an m = 1 call (the
+    batched arms' bit-parity gate).  Matrix cores: a 5-row call holding row t first and four
+    other rows after it, so row t sits at another position among other rows."""
+    if not mc:
         return c.gpu(fg, qs=to_dev(c.qs[t:t + 1]), d=to_dev(c.d[t:t + 1]), m=1)[0]
     idx = [t] + [(t + k) % c.m for k in range(1, 5)]
-    return c.gpu(fg, qs=to_dev(c.qs[idx]), d=to_dev(c.d[idx]), m=5)[0]
+    return c.gpu(fg, qs=to_dev(c.qs[idx]), d=to_dev(c.d[idx]), m=5, mc=True)[0]
 
 
 # m > 1 shares each weight pass between up to 8 activation rows (fewer beyond in_f = 8192);
 # m = 3, 5 and 11 leave rows of the last weight pass unused, 11 takes two passes.  Each row
-# of an m-row call is bit-identical to the same row computed alone: to an m = 1 call on the
-# vector path, and on the matrix cores (m >= 3) to that row at another position among other
-# rows.
+# of an m-row call is bit-identical to an m = 1 call on that row.
 @pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("kind", KINDS)
 def test_gemv_m_rows_bit_identical_per_row(fg, kind, out_f, in_f):
@@ -170,9 +164,25 @@ def test_gemv_m_rows_bit_identical_per_row(fg, kind, out_f, in_f):
         case(f"{kind} m={m} out_f={out_f} in_f={in_f}")
         y = c.gpu(fg, qs=to_dev(c.qs[:m]), d=to_dev(c.d[:m]), m=m)
         for t in range(m):
-            y1 = row_reference(fg, c, t, m)
+            y1 = row_reference(fg, c, t)
             assert y[t].tobytes() == y1.tobytes(), (m, t)
     # the last call (m = 11, two weight passes) against the oracle at every output
+    yo, A = c.oracle_all()
+    _assert_close(y, yo, A)
+
+
+# The matrix-core entry points at the same shapes: each row of an m-row call is bit-identical
+# to that row at another position among other rows, and every output of the last call is
+# within the parity bar of the oracle.
+@pytest.mark.parametrize("out_f,in_f", [(17408, 5120), (5120, 17408)])
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_matrix_core_rows_bit_identical_across_calls(fg, kind, out_f, in_f):
+    c = Case(kind, out_f, in_f, 11)
+    for m in (1, 2, 3, 4, 5, 8, 11):
+        case(f"{kind} matrix cores m={m} out_f={out_f} in_f={in_f}")
+        y = c.gpu(fg, qs=to_dev(c.qs[:m]), d=to_dev(c.d[:m]), m=m, mc=True)
+        for t in range(m):
+            assert y[t].tobytes() == row_reference(fg, c, t, mc=True).tobytes(), (m, t)
     yo, A = c.oracle_all()
     _assert_close(y, yo, A)
 
@@ -180,20 +190,20 @@ def test_gemv_m_rows_bit_identical_per_row(fg, kind, out_f, in_f):
 # The matrix-core kernel at its edges: in_f not a multiple of its 256-column step or of the
 # 1 KiB span of the 4 waves that share a row group (so some waves have no columns), rows
 # from one step to 65536 columns, out_f not a multiple of a wave's 16 rows, block-128 grids
-# with several row tiles, m = 3 (the smallest it takes), 8 (one full pass), 9 and 17 (a last
-# pass of one row), 16 (two full passes).  Rows of more than 8192 columns take the 8-way
-# column split.
+# with several row tiles, m = 1 and 2 (most of the 8 columns empty), 3, 8 (one full pass), 9
+# and 17 (a last pass of one row), 16 (two full passes).  Rows of more than 8192 columns take
+# the 8-way column split.
 MFMA_SHAPES = [(1, 32), (17, 288), (100, 1056), (200, 4128), (129, 8160), (65, 8192),
                (33, 8224), (300, 5120), (40, 17408), (9, 65536)]
 
 
-@pytest.mark.parametrize("m", [3, 5, 8, 9, 16, 17])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 16, 17])
 @pytest.mark.parametrize("out_f,in_f", MFMA_SHAPES)
 @pytest.mark.parametrize("kind", ["e4m3", "blk128"])
 def test_gemv_matrix_core_shapes_match_oracle(fg, kind, out_f, in_f, m):
     case(f"{kind} matrix cores out_f={out_f} in_f={in_f} m={m}")
     c = Case(kind, out_f, in_f, m)
-    y = c.gpu(fg)
+    y = c.gpu(fg, mc=True)
     yo, A = c.oracle()
     _assert_close(y, yo, A)
 
@@ -206,18 +216,19 @@ Q8_MFMA_SHAPES = [(1, 256), (17, 512), (100, 1280), (200, 4352), (65, 8192), (33
                   (300, 5120), (40, 17408), (9, 65536)]
 
 
-@pytest.mark.parametrize("m", [3, 5, 8, 9, 16, 17])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 16, 17])
 @pytest.mark.parametrize("out_f,in_f", Q8_MFMA_SHAPES)
 def test_gemv_q8_0_matrix_core_shapes_match_oracle(fg, out_f, in_f, m):
     case(f"q8_0 matrix cores out_f={out_f} in_f={in_f} m={m}")
     c = Case("q8_0", out_f, in_f, m)
-    y = c.gpu(fg)
+    y = c.gpu(fg, mc=True)
     yo, A = c.oracle()
     _assert_close(y, yo, A)
 
 
 # Beyond the matrix-core kernels' limit (a row stride of 64 MiB or more, where 16 rows'
-# offsets would leave 32 bits) several rows take the vector path, bit-identical to m=1.
+# offsets would leave 32 bits) the *_mc entry points run the vector kernels, bit-identical to
+# m=1.
 @pytest.mark.parametrize("kind", KINDS)
 def test_gemv_vector_path_beyond_the_matrix_core_limits(fg, kind):
     case(f"{kind} m=8 with a 64 MiB row stride")
@@ -228,7 +239,7 @@ def test_gemv_vector_path_beyond_the_matrix_core_limits(fg, kind):
     flat = torch.zeros((out_f - 1) * rb + nbytes, dtype=torch.uint8, device=dev())
     for r in range(out_f):
         flat[r * rb:r * rb + nbytes] = torch.from_numpy(c.W[r]).to(dev())
-    y = c.gpu(fg, Wd=flat, row_bytes=rb)
+    y = c.gpu(fg, Wd=flat, row_bytes=rb, mc=True)
     yo, A = c.oracle()
     _assert_close(y, yo, A)
     for t in range(m):
@@ -237,10 +248,10 @@ def test_gemv_vector_path_beyond_the_matrix_core_limits(fg, kind):
     vec, mat = (("k_gemv_q8_0_fast", "k_gemv_q8_0_mfma") if kind == "q8_0"
                 else ("k_gemv_e4m3<", "k_gemv_e4m3_mfma<"))
     rbf = (lambda n: n // 32 * 34) if kind == "q8_0" else (lambda n: n)
-    assert fg.gemv_launch_info(kind, rb, m, in_f, out_f)["kernel"].startswith(vec)
-    assert fg.gemv_launch_info(kind, rbf(in_f), m, in_f, out_f)["kernel"].startswith(mat)
-    assert fg.gemv_launch_info(kind, rbf(65536), m, 65536, out_f)["kernel"].startswith(mat)
-    assert fg.gemv_launch_info(kind, rbf(in_f), 2, in_f, out_f)["kernel"].startswith(vec)
+    assert fg.gemv_launch_info(kind + "_mc", rb, m, in_f, out_f)["kernel"].startswith(vec)
+    assert fg.gemv_launch_info(kind + "_mc", rbf(in_f), m, in_f, out_f)["kernel"].startswith(mat)
+    assert fg.gemv_launch_info(kind + "_mc", rbf(65536), m, 65536, out_f)["kernel"].startswith(mat)
+    assert fg.gemv_launch_info(kind, rbf(in_f), m, in_f, out_f)["kernel"].startswith(vec)
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -248,9 +259,9 @@ def test_gemv_matrix_core_rows_independent_of_order(fg, kind):
     # the same 8 rows in reverse order give each row the same bits
     case(f"{kind} matrix cores, rows reversed")
     c = Case(kind, 300, 5120, 8)
-    y = c.gpu(fg)
+    y = c.gpu(fg, mc=True)
     rev = list(range(7, -1, -1))
-    yr = c.gpu(fg, qs=to_dev(c.qs[rev]), d=to_dev(c.d[rev]))
+    yr = c.gpu(fg, qs=to_dev(c.qs[rev]), d=to_dev(c.d[rev]), mc=True)
     assert y.tobytes() == yr[rev].tobytes()
 
 
@@ -263,7 +274,7 @@ def test_gemv_matrix_core_padded_row_stride(fg, kind):
     Wp = np.zeros((out_f, c.row_bytes + pad), dtype=np.uint8)
     Wp[:, :c.row_bytes] = c.W
     Wp[:, c.row_bytes:] = 0x7F  # NaN codes, never read
-    y = c.gpu(fg, Wd=to_dev(Wp), row_bytes=c.row_bytes + pad)
+    y = c.gpu(fg, Wd=to_dev(Wp), row_bytes=c.row_bytes + pad, mc=True)
     yo, A = c.oracle()
     _assert_close(y, yo, A)
 
@@ -347,7 +358,12 @@ def test_max_m(fg, kind):
     yo, A = c.oracle()
     _assert_close(y, yo, A)
     for t in (0, 1, 7, 8, 32767, m - 2, m - 1):
-        assert row_reference(fg, c, t, m).tobytes() == y[t].tobytes(), f"row {t}"
+        assert row_reference(fg, c, t).tobytes() == y[t].tobytes(), f"row {t}"
+    # the matrix-core entry point over the same 65535 rows (8192 passes of 8)
+    y = c.gpu(fg, mc=True)
+    _assert_close(y, yo, A)
+    for t in (0, 7, 8, m - 1):
+        assert row_reference(fg, c, t, mc=True).tobytes() == y[t].tobytes(), f"row {t}"
 
 
 def test_bad_arguments_raise_and_launch_nothing(fg):
@@ -412,8 +428,9 @@ def test_graph_replays_match_eager(fg):
 
 
 def test_graph_replays_of_the_other_entry_points(fg):
-    # The two-launch chains, the SiLU-gated producer, m = 4 rows and the requantiser under
-    # graph replay: every replay, with eager work between replays, reproduces the eager bytes.
+    # The two-launch chains, the SiLU-gated producer, m = 4 rows (plain and matrix-core
+    # entry points) and the requantiser under graph replay: every replay, with eager work
+    # between replays, reproduces the eager bytes.
     case("graph replay of chains, silu producer, m = 4 and requant")
     in_f, out_f = 2048, 384
     x = to_dev(synth.x_rows(in_f, 4))
@@ -429,7 +446,9 @@ def test_graph_replays_of_the_other_entry_points(fg):
     y = torch.empty((4, out_f), device=dev())
     Wq = torch.empty(out_f * in_f // 32 * 34, dtype=torch.uint8, device=dev())
     yq = torch.empty((4, out_f), device=dev())
-    outs = [z, qs, d, h, hq, hd, y, Wq, yq]
+    ymc = torch.empty((4, out_f), device=dev())
+    yqmc = torch.empty((4, out_f), device=dev())
+    outs = [z, qs, d, h, hq, hd, y, Wq, yq, ymc, yqmc]
 
     def run():
         fg.rms_norm_f32(x, w, z, in_f, 4)
@@ -440,6 +459,9 @@ def test_graph_replays_of_the_other_entry_points(fg):
         fg.requant_e4m3_blk128_q8_0(c.Wd, c.row_bytes, c.gd, c.grid.shape[1], Wq,
                                     in_f // 32 * 34, in_f, out_f)
         fg.gemv_q8_0_q81(Wq, in_f // 32 * 34, qs, d, yq, 4, in_f, out_f)
+        fg.gemv_e4m3_blk128_q81_mc(c.Wd, c.row_bytes, c.gd, c.grid.shape[1], qs, d, ymc, 4,
+                                   in_f, out_f)
+        fg.gemv_q8_0_q81_mc(Wq, in_f // 32 * 34, qs, d, yqmc, 4, in_f, out_f)
 
     run()
     eager = [host(t).copy() for t in outs]
