@@ -256,8 +256,8 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
         wlo[r] = int4_t{w[0], lo_ge2 ? w[1] : 0, lo_ge3 ? w[2] : 0, lo_4 ? w[3] : 0};
         whi[r] = int4_t{0, lo_ge2 ? 0 : w[1], lo_ge3 ? 0 : w[2], lo_4 ? 0 : w[3]};
       }
-      // Activation row tt's chunk and scale from LDS; row tt + 1 is read while row tt is
-      // multiplied, so the LDS latency is not paid once per row.
+      // Activation row tt's chunk and scale from LDS, read ahead of its multiply (below), so
+      // the LDS latency is not paid once per row.
       auto read_row = [&](int tt, int4_t &a, float &da, float &da0) {
         const unsigned char *arow = lds + tt * row_lds;
         a = *reinterpret_cast<const int4_t *>(arow + win * kWinBytes + lds_lane);
@@ -276,16 +276,22 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
           hw0[r] = d0 ? hw[r] : (d1 ? g1 : g2);
         }
       }
-      int4_t abuf[2];
-      float dbuf[2], d0buf[2];
-      read_row(0, abuf[0], dbuf[0], d0buf[0]);
+      // Up to 4 rows: all their chunks are read before the first is multiplied; more rows:
+      // one row ahead (registers).
+      constexpr int NB = MT <= 4 ? MT : 2;
+      int4_t abuf[NB];
+      float dbuf[NB], d0buf[NB];
+#pragma unroll
+      for (int j = 0; j + 1 < NB; ++j) read_row(j, abuf[j], dbuf[j], d0buf[j]);
 #pragma unroll
       for (int tt = 0; tt < MT; ++tt) {
-        if (tt + 1 < MT) read_row(tt + 1, abuf[(tt + 1) & 1], dbuf[(tt + 1) & 1], d0buf[(tt + 1) & 1]);
-        const int4_t a = abuf[tt & 1];
+        if (tt + NB - 1 < MT)
+          read_row(tt + NB - 1, abuf[(tt + NB - 1) % NB], dbuf[(tt + NB - 1) % NB],
+                   d0buf[(tt + NB - 1) % NB]);
+        const int4_t a = abuf[tt % NB];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          const float H = hw[r] * dbuf[tt & 1];
+          const float H = hw[r] * dbuf[tt % NB];
           float h1 = 0.0f, h2 = 0.0f;
           if constexpr (MT == 1) {
             h1 = wave_shr1(H);   // scale of chunk c - 1
@@ -313,7 +319,7 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
           if constexpr (MT == 1) {
             S0 = d0 ? H : (d1 ? h1 : h2);
           } else {
-            S0 = hw0[r] * d0buf[tt & 1];
+            S0 = hw0[r] * d0buf[tt % NB];
           }
           acc[tt][r] = fmaf((float)s_lo, S0, acc[tt][r]);
           acc[tt][r] = fmaf((float)s_hi, H, acc[tt][r]);
