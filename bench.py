@@ -40,8 +40,8 @@ Q8_PATTERNS = ("rows_816", "rows_aligned", "line_windows")
 ARMS = ["e4m3", "blk128", "q8_0"]
 SCALE = 2.0 ** -4
 EPS = 1e-6
-# The projection shape sheets of the bench page ([out_f, in_f], label): the 27B sheet carries
-# the verdict, the 1.7B sheet is reported alongside.
+# The projection shape sheets of the bench page ([out_f, in_f], label): the 27B sheet decides
+# the page's geomean comparison, the 1.7B sheet is reported alongside.
 SHEETS = {
     "27b": [(12288, 5120, "q_proj"), (1024, 5120, "k/v_proj"), (5120, 6144, "o_proj"),
             (17408, 5120, "gate/up_proj"), (5120, 17408, "down_proj"), (5120, 5120, "square-ref")],
