@@ -322,6 +322,26 @@ def test_q8_0_unaligned_rows_take_the_generic_path(fg, in_f):
     assert y.tobytes() == c.gpu(fg, Wd=buf[2:]).tobytes()
 
 
+# Q8_0 row layouts the matrix-core kernel does not take (in_f % 256 != 0, or W only 2-byte
+# aligned): the matrix-core entry point runs the plain entry point's kernels, so its rows are
+# byte-identical to the plain call's, for m = 1 and for several rows.
+@pytest.mark.parametrize("in_f,offset", [(288, 0), (1056, 0), (2048, 2)])
+@pytest.mark.parametrize("m", [1, 5])
+def test_q8_0_matrix_core_entry_falls_back_off_its_layouts(fg, in_f, offset, m):
+    case(f"q8_0 matrix-core entry fallback in_f={in_f} offset={offset} m={m}")
+    c = Case("q8_0", 77, in_f, m)
+    flat = np.zeros(c.W.size + 16, dtype=np.uint8)
+    flat[offset:offset + c.W.size] = c.W.reshape(-1)
+    Wd = to_dev(flat)[offset:]
+    y = c.gpu(fg, Wd=Wd, mc=True)
+    assert y.tobytes() == c.gpu(fg, Wd=Wd).tobytes()
+    yo, A = c.oracle()
+    _assert_close(y, yo, A)
+    kern = fg.gemv_launch_info("q8_0_mc", c.row_bytes, m, in_f, 77,
+                               w_align=2 if offset else 256)["kernel"]
+    assert "mfma" not in kern
+
+
 @pytest.mark.parametrize("kind", ["e4m3", "blk128", "q8_0"])
 def test_padded_row_stride(fg, kind):
     case(f"{kind} padded row stride")
