@@ -103,10 +103,21 @@ __host__ __device__ constexpr size_t fast_lds_bytes(int in_f, int mt) {
   return (size_t)mt * row_lds_bytes(in_f) + kSinkBytes;
 }
 
-// Wave-wide shift right by one lane (DPP wave_shr:1); lane 0 receives 0.
+// Wave-wide shift right by one lane (DPP wave_shr:1); lane 0 receives 0 (bound_ctrl: a lane
+// whose source is out of range reads zero, so no zero has to be moved into the destination
+// first).
 __device__ __forceinline__ float wave_shr1(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               kWaveShr1, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                            kWaveShr1, 0xF, 0xF, true));
+}
+
+// Signed 4 x int8 dot product plus c.  The clamp bit keeps the compiler on the three-operand
+// v_dot4_i32_i8: without it the accumulator is tied to the destination (v_dot4c), and every
+// partial sum that is also used on its own costs a copy.  The sums here stay far inside int32
+// (at most 16 * 128 * 127 in magnitude per chunk), so the clamp never acts and the result is
+// the exact integer.
+__device__ __forceinline__ int dot4(int a, int b, int c) {
+  return __builtin_amdgcn_sdot4(a, b, c, true);
 }
 
 template <class C>
@@ -300,20 +311,20 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
           int s_lo, s_hi;
           if constexpr (MT == 1) {
             const int4_t w = wb[u][r];
-            const int t1 = __builtin_amdgcn_sdot4(w[0], a[0], 0, false);
-            const int t2 = __builtin_amdgcn_sdot4(w[1], a[1], t1, false);
-            const int t3 = __builtin_amdgcn_sdot4(w[2], a[2], t2, false);
-            const int t4 = __builtin_amdgcn_sdot4(w[3], a[3], t3, false);
+            const int t1 = dot4(w[0], a[0], 0);
+            const int t2 = dot4(w[1], a[1], t1);
+            const int t3 = dot4(w[2], a[2], t2);
+            const int t4 = dot4(w[3], a[3], t3);
             s_lo = lo_4 ? t4 : (lo_ge3 ? t3 : (lo_ge2 ? t2 : t1));
             s_hi = t4 - s_lo;
           } else {
-            s_lo = __builtin_amdgcn_sdot4(wlo[r][0], a[0], 0, false);
-            s_lo = __builtin_amdgcn_sdot4(wlo[r][1], a[1], s_lo, false);
-            s_lo = __builtin_amdgcn_sdot4(wlo[r][2], a[2], s_lo, false);
-            s_lo = __builtin_amdgcn_sdot4(wlo[r][3], a[3], s_lo, false);
-            s_hi = __builtin_amdgcn_sdot4(whi[r][1], a[1], 0, false);
-            s_hi = __builtin_amdgcn_sdot4(whi[r][2], a[2], s_hi, false);
-            s_hi = __builtin_amdgcn_sdot4(whi[r][3], a[3], s_hi, false);
+            s_lo = dot4(wlo[r][0], a[0], 0);
+            s_lo = dot4(wlo[r][1], a[1], s_lo);
+            s_lo = dot4(wlo[r][2], a[2], s_lo);
+            s_lo = dot4(wlo[r][3], a[3], s_lo);
+            s_hi = dot4(whi[r][1], a[1], 0);
+            s_hi = dot4(whi[r][2], a[2], s_hi);
+            s_hi = dot4(whi[r][3], a[3], s_hi);
           }
           float S0;
           if constexpr (MT == 1) {
