@@ -51,6 +51,7 @@ SHEETS = {
 M_ROWS = (1, 2, 4, 8)   # small-batch activation rows, timed at SHAPE_M
 MAX_M = max(M_ROWS)
 SHAPE_M = (17408, 5120)
+GEMV_FIT_OUT_F = (4096, 8192, 17408, 32768)  # out_f of the m = 1 GEMV fit, in_f = 5120
 
 
 # Spin before a queue of individually timed launches: ~10 ms at the shader clock, longer than
@@ -896,6 +897,29 @@ def main() -> int:
         read_fit = dict(read_patterns[best_pat], pattern=best_pat)
         log(f"read ceiling: best pattern at 89 MB {best_pat}: steady {read_fit['steady_GBs']} "
             f"GB/s ({read_fit['steady_pct_peak']}%), fixed {read_fit['fixed_us']} us per launch")
+
+    # The m = 1 GEMVs fitted the same way, over out_f at in_f = 5120 (one launch shape for
+    # every out_f): t = fixed + weight bytes / steady.  Set beside the read patterns' fit, this
+    # splits each GEMV's distance from the best read into a per-launch part and a per-byte part.
+    gemv_fit = {}
+    if not (args.kernels_only or args.no_read_patterns):
+        for a in ("e4m3", "q8_0"):
+            if a not in arms:
+                continue
+            qs, d = producer((5120, 5120)) if (5120, 5120) in prod else (None, None)
+            if qs is None:
+                break
+            pts = []
+            for out_f in GEMV_FIT_OUT_F:
+                obj = Arm(fg, torch, a, out_f, 5120, dev)
+                us, _ = graph_us(lambda i: obj.launch(qs, d), max(args.kernel_iters // 2, obj.copies),
+                                 reps=3)
+                pts.append((weight_bytes(a, out_f, 5120), round(us, 3)))
+                del obj
+                torch.cuda.empty_cache()
+            gemv_fit[a] = dict(fit_read_ceiling(pts), in_f=5120, out_f=list(GEMV_FIT_OUT_F))
+            log(f"gemv fit {a:5s}: " + ", ".join(f"{b / 1e6:.1f} MB {t:.2f} us" for b, t in pts)
+                + f"; steady {gemv_fit[a]['steady_GBs']} GB/s, fixed {gemv_fit[a]['fixed_us']} us")
     for k, v in detail.items():
         shape = k.split("@")[1]
         if shape in ceiling:
@@ -1081,7 +1105,7 @@ def main() -> int:
                    "eps": EPS, "e4m3_scale": SCALE},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "eager_ms_per_step": round(eager_ms, 4), "host_wall_ms_per_step": round(wall_ms, 4),
-        "gemv": detail, "read_ceiling": ceiling, "read_fit": read_fit,
+        "gemv": detail, "read_ceiling": ceiling, "read_fit": read_fit, "gemv_fit": gemv_fit,
         "read_patterns": read_patterns, "q8_0_read_ceiling": q8_ceiling, "fixed_cost": fixed,
         "m_rows": m_rows, "m_rows_matrix_cores": m_rows_mc, "sheets": sheets,
         "requant": requant,
