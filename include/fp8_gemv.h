@@ -202,7 +202,7 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
  * up to 8 activation rows per instruction, one q8_1 block (K = 32) at a time.  Opt-in: at
  * m >= 3 the vector kernels of the plain entry points are bound by their per-row arithmetic,
  * not by the weight stream, and these keep the cost nearly flat in m (17408 x 5120: m = 8
- * takes 1.4-1.5x m = 1, against 3x on the vector kernels).
+ * takes 1.4-1.5x m = 1, against 2.8-3x on the vector kernels).
  * What they give up is the bit-parity gate of the batched arms: each block's sum is formed by
  * the matrix core and the block sums are added in a fixed order of their own, so a row agrees
  * with the plain entry point to rounding (within the parity tolerance, 1e-5 of the sum of the
