@@ -96,6 +96,19 @@ inline hipError_t set_lds_limit_once(const void *kernel, size_t bytes,
     done[dev].store(true, std::memory_order_release);
   return e;
 }
+// CUs of the current device, cached per device (256 if it cannot be read: it only sizes the
+// grids of the persistent launches, and every grid size computes the same result).
+inline int cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+    c = 256;
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
 }  // namespace fp8gemv
 
 // -------------------------------------------------------------- launch descriptions ----

@@ -35,7 +35,11 @@
 // Several activation rows (MT per workgroup, grid.y = ceil(m / MT)) share one weight pass:
 // each weight chunk is decoded once and multiplied into every row with the same operations
 // in the same order as for MT = 1, and every launch shape of an in_f range splits rows the
-// same way, so row t of an m-row call is bit-identical to an m=1 call on that row.
+// same way, so row t of an m-row call is bit-identical to an m=1 call on that row.  The
+// launches for 3-8 rows of up to 8192 columns are persistent: as many workgroups as fit on the
+// device stage their activation rows once, and each wave then takes groups of RPW weight rows
+// in turn, so that the staging is not repeated per row group and the last groups spread over
+// all CUs instead of leaving a partial round of workgroups.
 #include "common.hpp"
 
 namespace fp8gemv {
@@ -97,6 +101,18 @@ struct Cfg {
   static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, K = K_, KD = KD_, WPE = WPE_;
   static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
   static constexpr int MT = MT_;
+  // The launches for 3-8 activation rows (short rows, whole rows per wave) are persistent:
+  // as many workgroups as fit on the device at once, whose waves loop over row groups.  (With
+  // 2 rows the staging is cheap and the launch already fills the device evenly; there the
+  // block-128 grid value, fetched per window and row, cost more than the loop saved.)
+  static constexpr bool PERSIST = MT_ >= 4 && SPLIT_ == 1;
+  // workgroups that fit on one CU: WPE waves per SIMD, and the LDS of MT staged rows
+  static constexpr int wgs_per_cu(int in_f) {
+    const int by_waves = 4 * WPE_ / WAVES_;
+    const int lds = (int)(MT_ * act_lds_bytes(in_f) + kSinkBytes);
+    const int by_lds = (160 * 1024) / ((lds + 1023) / 1024 * 1024);
+    return by_waves < by_lds ? by_waves : by_lds;
+  }
   static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
   static constexpr bool DB = DB_;
   static constexpr int THREADS = WAVES * kWave;
@@ -116,6 +132,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   constexpr int RPW = C::RPW, U = C::U, K = C::K, KD = C::KD, NTH = C::THREADS, MT = C::MT;
   constexpr int SPLIT = C::SPLIT;
   static_assert(C::WAVES % SPLIT == 0 && 128 % C::ROWS == 0, "a workgroup's rows lie in one tile");
+  static_assert(128 % RPW == 0, "a wave's rows lie in one tile");
   extern __shared__ __align__(16) unsigned char lds[];
   const int nwin = num_windows(in_f);
   const size_t row_lds = act_lds_bytes(in_f);  // one staged activation row
@@ -123,7 +140,16 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   const int t0 = blockIdx.y * MT;  // first activation row of this workgroup
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
-  const int rbase = (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
+  // PERSIST (the 8-row launch): one workgroup per CU stages the activation rows once and its
+  // waves then take groups of RPW weight rows in turn, group g by wave g mod (waves of the
+  // grid), numbered so that consecutive groups fall on different workgroups.  Every row is
+  // still computed by one wave with the operations of m = 1.
+  constexpr bool PERSIST = C::PERSIST;
+  static_assert(!PERSIST || SPLIT == 1, "a persistent wave owns whole rows");
+  const int ngroups = (out_f + RPW - 1) / RPW;
+  const int gstride = (int)gridDim.x * C::WAVES;
+  int grp = wave * (int)gridDim.x + (int)blockIdx.x;
+  int rbase = PERSIST ? grp * RPW : (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
   const int part = wave % SPLIT;
   const int wbeg = part * nwin / SPLIT, wend = (part + 1) * nwin / SPLIT;  // this wave's windows
   const int nb = in_f / 32;
@@ -142,7 +168,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
 #pragma unroll
     for (int k = 0; k < KD; ++k) dv[tt][k] = buf_load_f32(drs, (uint32_t)(threadIdx.x + k * NTH) * 4);
   }
-  if (BLK) {
+  if (BLK && !PERSIST) {
     // Grid row of this workgroup (its rows all lie in one 128-row tile); clamped so a
     // workgroup past the last row still reads inside the grid.
     const int rfirst = blockIdx.x * C::ROWS;
@@ -160,21 +186,42 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   // first in_f bytes (none for a row past out_f), so out-of-range windows read as zeros.
   rsrc_t wrs[RPW];
   bool rok[RPW];
+  rsrc_t grs = buf_rsrc(grid, 0u);  // PERSIST, block-128: the grid row of the current rows
+  auto setup_rows = [&]() {
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    rok[r] = rbase + r < out_f;
-    // wbeg < nwin, so wbeg * 1024 < in_f and the record count is never negative
-    const int lim = in_f < wend * kWinCols ? in_f : wend * kWinCols;
-    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * kWinCols,
-                      rok[r] ? (uint32_t)(lim - wbeg * kWinCols) : 0u);
-  }
+    for (int r = 0; r < RPW; ++r) {
+      rok[r] = rbase + r < out_f;
+      // wbeg < nwin, so wbeg * 1024 < in_f and the record count is never negative
+      const int lim = in_f < wend * kWinCols ? in_f : wend * kWinCols;
+      wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * kWinCols,
+                        rok[r] ? (uint32_t)(lim - wbeg * kWinCols) : 0u);
+    }
+    if constexpr (PERSIST && BLK) {
+      // RPW divides 128, so a group's rows lie in one 128-row tile
+      const bool ok = rbase < out_f;
+      grs = buf_rsrc(grid + (int64_t)(ok ? rbase / 128 : 0) * grid_cols,
+                     ok ? (uint32_t)grid_cols * 4 : 0u);
+    }
+  };
+  setup_rows();
+  // Loads are issued unconditionally: past the row they read zeros and no memory.  With
+  // PERSIST and block-128, each window's grid value (the lane's 128-column tile, window * 8 +
+  // lane / 8) comes in with the window's weights.
+  auto load = [&](int4_t (&wb)[U][RPW], float (&gb)[U], int w0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u - wbeg) * kWinCols + lane * 16));
+      if constexpr (PERSIST && BLK)
+        gb[u] = buf_load_f32(grs, (uint32_t)(((w0 + u) * (kWinCols / 128) + lane / 8) * 4));
+      else
+        gb[u] = 1.0f;
+    }
+  };
   int4_t wv[U][RPW];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      wv[u][r] = buf_load16_stream(wrs[r], (uint32_t)(u * kWinCols + lane * 16));
-  }
+  float gv1[U];
+  load(wv, gv1, wbeg);
 
   // 3. stage the activation rows (f16) and their scales in LDS; zeros past in_f.  Threads
   // past the staged range write into the sink instead of branching around the store.
@@ -213,7 +260,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   for (int tt = 0; tt < MT; ++tt)
 #pragma unroll
     for (int r = 0; r < RPW; ++r) acc[tt][r] = 0.0f;
-  auto compute = [&](const int4_t (&wb)[U][RPW], int w0) {
+  auto compute = [&](const int4_t (&wb)[U][RPW], const float (&gb)[U], int w0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int win = w0 + u;
@@ -233,6 +280,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
           *reinterpret_cast<int4_t *>(a + 4) =
               *reinterpret_cast<const int4_t *>(act + base + kWinCols / 2);
           sc = dsc[col / 32];
+          if constexpr (PERSIST && BLK) sc = sc * gb[u];
         };
         half2_t a[2][8];
         float sc[2];
@@ -247,28 +295,21 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
       }
     }
   };
-  // Loads are issued unconditionally: past the row they read zeros and no memory.
-  auto load = [&](int4_t (&wb)[U][RPW], int w0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-        wb[u][r] = buf_load16_stream(wrs[r], (uint32_t)((w0 + u - wbeg) * kWinCols + lane * 16));
-    }
-  };
+  for (;;) {
   if constexpr (C::DB) {
     int4_t wv2[U][RPW];
+    float gv2[U];
     for (int w0 = wbeg; w0 < wend; w0 += 2 * U) {
-      load(wv2, w0 + U);
-      compute(wv, w0);
+      load(wv2, gv2, w0 + U);
+      compute(wv, gv1, w0);
       if (w0 + U >= wend) break;
-      load(wv, w0 + 2 * U);
-      compute(wv2, w0 + U);
+      load(wv, gv1, w0 + 2 * U);
+      compute(wv2, gv2, w0 + U);
     }
   } else {
     for (int w0 = wbeg; w0 < wend; w0 += U) {
-      compute(wv, w0);
-      load(wv, w0 + U);
+      compute(wv, gv1, w0);
+      load(wv, gv1, w0 + U);
     }
   }
 
@@ -282,6 +323,17 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
           y[(int64_t)(t0 + tt) * out_f + rbase + r] = BLK ? s : s * scale;
       }
     }
+    if constexpr (!PERSIST) break;
+    // the next group of this wave, if any (wave-uniform)
+    grp += gstride;
+    if (grp >= ngroups) break;
+    rbase = grp * RPW;
+    setup_rows();
+    load(wv, gv1, wbeg);
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) acc[tt][r] = 0.0f;
   } else {
     // the SPLIT partial sums of a row meet in LDS and are added in part order
     __shared__ float psum[MT][C::WAVES * RPW];
@@ -306,6 +358,22 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
         }
       }
     }
+    break;
+  }
+  }
+}
+
+// Workgroups along x: one per ROWS rows, or for a persistent launch as many as fit on the
+// device at once (at most one per WAVES row groups), so one round covers the grid.
+template <class C>
+unsigned grid_x_for(int out_f, int in_f) {
+  if constexpr (C::PERSIST) {
+    const int groups = (out_f + C::RPW - 1) / C::RPW;
+    const int want = (groups + C::WAVES - 1) / C::WAVES;
+    const int cap = cu_count() * C::wgs_per_cu(in_f);
+    return (unsigned)(want < cap ? want : cap);
+  } else {
+    return (unsigned)((out_f + C::ROWS - 1) / C::ROWS);
   }
 }
 
@@ -319,7 +387,7 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
   const hipError_t e = set_lds_limit_once(reinterpret_cast<const void *>(kern),
                                           want < kLdsBytes ? want : kLdsBytes, lds_set);
   if (e != hipSuccess) return e;
-  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, (m + C::MT - 1) / C::MT);
+  const dim3 g(grid_x_for<C>(out_f, in_f), (m + C::MT - 1) / C::MT);
   hipLaunchKernelGGL(kern, g, dim3(C::THREADS), C::MT * act_lds_bytes(in_f) + kSinkBytes, s, W,
                      row_bytes, scale, grid, grid_cols, qs, d, y, m, in_f, out_f);
   return hipGetLastError();
@@ -404,7 +472,7 @@ LaunchDesc describe_gemv_e4m3(bool blk128, int64_t row_bytes, int m, int in_f, i
   return with_cfg(m, in_f, [&](auto tag) {
     using C = typename decltype(tag)::type;
     LaunchDesc r;
-    r.grid_x = (unsigned)((out_f + C::ROWS - 1) / C::ROWS);
+    r.grid_x = grid_x_for<C>(out_f, in_f);
     r.grid_y = (unsigned)((m + C::MT - 1) / C::MT);
     r.threads = C::THREADS;
     r.lds = (unsigned)(C::MT * act_lds_bytes(in_f) + kSinkBytes);

@@ -42,7 +42,9 @@
 // multiplies it by its own d_a there; that is the product the scale's own lane forms for
 // MT = 1, so the bits are the same.)  Every launch shape
 // of an in_f range splits rows the same way, so each activation row of an m-row call is
-// bit-identical to an m=1 call on that row.
+// bit-identical to an m=1 call on that row.  The launches for 3-8 rows of up to 8192 columns
+// are persistent, as in the e4m3 stream: the device's resident workgroups stage their
+// activation rows once and their waves take groups of RPW weight rows in turn.
 #include "common.hpp"
 
 namespace fp8gemv {
@@ -77,6 +79,10 @@ struct QCfg {
   static constexpr int MT = MT_;
   static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
   static constexpr int ROWS = WAVES / SPLIT * RPW;  // rows per workgroup
+  // The launches for 3-8 activation rows are persistent: as many workgroups as fit on the
+  // device at once, whose waves loop over groups of RPW rows (the staging of the MT
+  // activation rows is paid once per workgroup, and the rows spread evenly over the waves).
+  static constexpr bool PERSIST = MT_ >= 4 && SPLIT_ == 1;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int MAX_IN_F = KQ * THREADS * 32;
   // the template arguments, for config_text
@@ -138,7 +144,15 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   const int t0 = blockIdx.y * MT;  // first activation row of this workgroup
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
-  const int rbase = (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
+  // PERSIST: group g of RPW rows belongs to wave g mod (waves of the grid), numbered so that
+  // consecutive groups fall on different workgroups; every row is still computed by one wave
+  // with the operations of m = 1.
+  constexpr bool PERSIST = C::PERSIST;
+  static_assert(!PERSIST || SPLIT == 1, "a persistent wave owns whole rows");
+  const int ngroups = (out_f + RPW - 1) / RPW;
+  const int gstride = (int)gridDim.x * C::WAVES;
+  int grp = wave * (int)gridDim.x + (int)blockIdx.x;
+  int rbase = PERSIST ? grp * RPW : (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
   const int part = wave % SPLIT;
   const int wbeg = part * nwin / SPLIT, wend = (part + 1) * nwin / SPLIT;  // this wave's windows
 
@@ -168,14 +182,17 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
   const uint32_t lane_off = lane < kWinLanes ? (uint32_t)lane * 16 : 0x40000000u;
   rsrc_t wrs[RPW];
   bool rok[RPW];
+  auto setup_rows = [&]() {
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    rok[r] = rbase + r < out_f;
-    // wbeg < nwin, so 816 * wbeg < row_used and the record count is never negative
-    const int lim = row_used < wend * kWinBytes ? row_used : wend * kWinBytes;
-    wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * kWinBytes,
-                      rok[r] ? (uint32_t)(lim - wbeg * kWinBytes) : 0u);
-  }
+    for (int r = 0; r < RPW; ++r) {
+      rok[r] = rbase + r < out_f;
+      // wbeg < nwin, so 816 * wbeg < row_used and the record count is never negative
+      const int lim = row_used < wend * kWinBytes ? row_used : wend * kWinBytes;
+      wrs[r] = buf_rsrc(W + (int64_t)(rok[r] ? rbase + r : 0) * row_bytes + (int64_t)wbeg * kWinBytes,
+                        rok[r] ? (uint32_t)(lim - wbeg * kWinBytes) : 0u);
+    }
+  };
+  setup_rows();
   int4_t wv[U][RPW];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -347,6 +364,7 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
         wb[u][r] = buf_load16_stream(wrs[r], lane_off + (uint32_t)((w0 + u - wbeg) * kWinBytes));
     }
   };
+  for (;;) {
   if constexpr (C::DB) {
     int4_t wv2[U][RPW];
     for (int w0 = wbeg; w0 < wend; w0 += 2 * U) {
@@ -372,6 +390,17 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
         if (lane == 0 && rok[r] && t0 + tt < m) y[(int64_t)(t0 + tt) * out_f + rbase + r] = s;
       }
     }
+    if constexpr (!PERSIST) break;
+    // the next group of this wave, if any (wave-uniform)
+    grp += gstride;
+    if (grp >= ngroups) break;
+    rbase = grp * RPW;
+    setup_rows();
+    load(wv, wbeg);
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) acc[tt][r] = 0.0f;
   } else {
     // the SPLIT partial sums of a row meet in LDS and are added in part order
     __shared__ float psum[MT][C::WAVES * RPW];
@@ -396,6 +425,8 @@ void k_gemv_q8_0_fast(const uint8_t *__restrict__ W, int64_t row_bytes,
         }
       }
     }
+    break;
+  }
   }
 }
 
@@ -430,6 +461,24 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q8_0_generic(
   if (lane == 0) y[(int64_t)t * out_f + row] = s;
 }
 
+// Workgroups along x: one per ROWS rows, or for a persistent launch as many as fit on the
+// device at once (WPE waves per SIMD and the LDS of the staged rows; at most one per WAVES row
+// groups), so one round covers the grid.
+template <class C>
+unsigned grid_x_for(int out_f, int in_f) {
+  if constexpr (C::PERSIST) {
+    const int groups = (out_f + C::RPW - 1) / C::RPW;
+    const int want = (groups + C::WAVES - 1) / C::WAVES;
+    const int by_waves = 4 * C::WPE / C::WAVES;
+    const int lds = (int)fast_lds_bytes(in_f, C::MT);
+    const int by_lds = (int)(kLdsBytes / ((lds + 1023) / 1024 * 1024));
+    const int cap = cu_count() * (by_waves < by_lds ? by_waves : by_lds);
+    return (unsigned)(want < cap ? want : cap);
+  } else {
+    return (unsigned)((out_f + C::ROWS - 1) / C::ROWS);
+  }
+}
+
 template <class C>
 hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, const float *d,
                        float *y, int m, int in_f, int out_f, hipStream_t s) {
@@ -439,7 +488,7 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
   const hipError_t e = set_lds_limit_once(reinterpret_cast<const void *>(kern),
                                           want < kLdsBytes ? want : kLdsBytes, lds_set);
   if (e != hipSuccess) return e;
-  const dim3 g((out_f + C::ROWS - 1) / C::ROWS, (m + C::MT - 1) / C::MT);
+  const dim3 g(grid_x_for<C>(out_f, in_f), (m + C::MT - 1) / C::MT);
   hipLaunchKernelGGL(kern, g, dim3(C::THREADS), fast_lds_bytes(in_f, C::MT), s, W, row_bytes, qs,
                      d, y, m, in_f, out_f);
   return hipGetLastError();
@@ -457,7 +506,7 @@ hipError_t launch_fast(const uint8_t *W, int64_t row_bytes, const int8_t *qs, co
 // computed in the same order whatever m is.
 using QSmall = QCfg<4, 1, 4, 1, 2, true>;                 // in_f <= 8192, m = 1
 using QSmallB2 = QCfg<4, 1, 3, 1, 2, true, 8, 1, 2>;      //               m = 2
-using QSmallB4 = QCfg<4, 1, 2, 1, 2, true, 6, 1, 4>;      //               m = 3..4
+using QSmallB4 = QCfg<4, 1, 2, 1, 2, true, 5, 1, 4>;      //               m = 3..4
 using QSmallB8 = QCfg<8, 2, 1, 1, 3, true, 4, 1, 8>;      //               m >= 5
 using QMid = QCfg<4, 1, 4, 3, 4, true>;                   // in_f <= 24576, m = 1
 using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 1, 2>;        //                m >= 2
@@ -531,7 +580,7 @@ LaunchDesc describe_gemv_q8_0(const uint8_t *W, int64_t row_bytes, int m, int in
     return with_cfg(m, in_f, [&](auto tag) {
       using C = typename decltype(tag)::type;
       LaunchDesc r;
-      r.grid_x = (unsigned)((out_f + C::ROWS - 1) / C::ROWS);
+      r.grid_x = grid_x_for<C>(out_f, in_f);
       r.grid_y = (unsigned)((m + C::MT - 1) / C::MT);
       r.threads = C::THREADS;
       r.lds = (unsigned)fast_lds_bytes(in_f, C::MT);

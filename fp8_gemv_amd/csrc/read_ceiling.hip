@@ -210,14 +210,6 @@ hipError_t launch_chunks(const uint8_t *p, int64_t bytes, uint32_t *sink, hipStr
                 WAVES * kWave, s, p, bytes, sink);
 }
 
-int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-    return 256;
-  return n;
-}
-
 }  // namespace
 
 hipError_t launch_read_bytes(const void *p, int64_t bytes, uint32_t *sink, hipStream_t s) {
