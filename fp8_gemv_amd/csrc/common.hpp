@@ -22,28 +22,37 @@ constexpr int kRowRor8 = 0x128;      // rotate right by 8 within each row of 16
 constexpr int kWaveShr1 = 0x138;     // shift right by one lane across the whole wave
 constexpr int kRowHalfMirror = 0x141;  // reverse lanes within each group of 8
 
-// Full row and bank masks, bound_ctrl off: every lane has a valid source for these patterns.
+// Full row and bank masks.  Every lane has a valid source for these patterns, so bound_ctrl
+// changes nothing here; it is set because it lets the compiler fold the move into the
+// instruction that consumes it (v_add_f32_dpp instead of v_mov_b32_dpp + v_add_f32).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over all 64 lanes.  Within each row of 16 lanes a DPP butterfly (xor 1, xor 2, then
-// rotations by 4 and 8) leaves the row sum in every lane; the four row sums are then read
-// from lanes 0, 16, 32, 48 and added in that fixed order.  The result is wave-uniform and
-// depends only on the lane values, never on timing.
+// rotations by 4 and 8) leaves the row sum r_k in the row's first lane (16k); the four row
+// sums are then added in the fixed order (r0 + r1) + (r2 + r3): v_permlane16_swap brings lane
+// 16 to lane 0 and lane 48 to lane 32, v_permlane32_swap then lane 32 to lane 0.  The result
+// is read from lane 0, so it is wave-uniform, and it depends only on the lane values.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<kQuadPerm1032>(v);
   v += dpp_f32<kQuadPerm2301>(v);
   v += dpp_f32<kRowRor4>(v);
   v += dpp_f32<kRowRor8>(v);
+  // Swapping a value with itself: element 0 keeps the even rows (lanes 0-15, 32-47) and
+  // element 1 holds the odd rows moved down (lane 0 <- 16, lane 32 <- 48).
   const int iv = __builtin_bit_cast(int, v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
-  return (r0 + r1) + (r2 + r3);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
+  // lane 0: r0 + r1; lane 32: r2 + r3
+  const float t = __builtin_bit_cast(float, (int)p16[0]) + __builtin_bit_cast(float, (int)p16[1]);
+  // element 0 keeps lanes 0-31, element 1 holds lanes 32-63 moved down (lane 0 <- 32)
+  const int it = __builtin_bit_cast(int, t);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(it, it, false, false);
+  // lane 0: (r0 + r1) + (r2 + r3)
+  const float u = __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), 0));
 }
 
 // ----------------------------------------------------------------------- loads ----
