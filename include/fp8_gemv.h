@@ -202,7 +202,7 @@ int gemv_e4m3_blk128_q81(const uint8_t *W, int64_t row_bytes, const float *grid,
  * up to 8 activation rows per instruction, one q8_1 block (K = 32) at a time.  Opt-in: at
  * m >= 3 the vector kernels of the plain entry points are bound by their per-row arithmetic,
  * not by the weight stream, and these keep the cost nearly flat in m (17408 x 5120: m = 8
- * takes 1.4-1.5x m = 1, against 2.8-3x on the vector kernels).
+ * takes 1.4-1.5x m = 1, against 2.0-2.6x on the vector kernels).
  * What they give up is the bit-parity gate of the batched arms: each block's sum is formed by
  * the matrix core and the block sums are added in a fixed order of their own, so a row agrees
  * with the plain entry point to rounding (within the parity tolerance, 1e-5 of the sum of the
@@ -331,9 +331,14 @@ int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_
  *               its alignment matters, for the Q8_0 fast-path choice)
  *   info        out: grid in workgroups (x = weight rows, y = activation-row passes), threads per
  *               workgroup, dynamic LDS bytes, the kernel family and its launch configuration as
- *               they appear in the demangled kernel symbol (static strings)
+ *               they appear in the demangled kernel symbol (static strings).  The launches for
+ *               3-8 activation rows of up to 8192 columns are persistent: their grid_x is the
+ *               workgroups that fit on the current device at once (its CU count, read once per
+ *               device; 256 CUs are assumed where it cannot be read), whose waves loop over the
+ *               weight rows.
  * Returns the argument checks of the GEMV (FP8GEMV_ERR_* as above, W and info must be
- * non-NULL) and FP8GEMV_ERR_SHAPE for an unknown container; touches no device.
+ * non-NULL) and FP8GEMV_ERR_SHAPE for an unknown container; reads the current device's CU
+ * count at most once, and touches no device memory.
  */
 #define FP8GEMV_Q8_0         0
 #define FP8GEMV_E4M3         1
