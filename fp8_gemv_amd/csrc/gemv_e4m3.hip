@@ -101,11 +101,11 @@ struct Cfg {
   static constexpr int WAVES = WAVES_, RPW = RPW_, U = U_, K = K_, KD = KD_, WPE = WPE_;
   static constexpr int SPLIT = SPLIT_;  // waves sharing one group of RPW rows (split over k)
   static constexpr int MT = MT_;
-  // The launches for 3-8 activation rows (short rows, whole rows per wave) are persistent:
-  // as many workgroups as fit on the device at once, whose waves loop over row groups.  (With
-  // 2 rows the staging is cheap and the launch already fills the device evenly; there the
-  // block-128 grid value, fetched per window and row, cost more than the loop saved.)
-  static constexpr bool PERSIST = MT_ >= 4 && SPLIT_ == 1;
+  // The launches for 4-8 staged activation rows are persistent: as many workgroups as fit on
+  // the device at once, whose waves loop over row groups.  (With 2 rows the staging is cheap
+  // and the launch already fills the device evenly; there the block-128 grid value, fetched
+  // per window and row, cost more than the loop saved.)
+  static constexpr bool PERSIST = MT_ >= 4;
   // workgroups that fit on one CU: WPE waves per SIMD, and the LDS of MT staged rows
   static constexpr int wgs_per_cu(int in_f) {
     const int by_waves = 4 * WPE_ / WAVES_;
@@ -140,16 +140,20 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
   const int t0 = blockIdx.y * MT;  // first activation row of this workgroup
   const int lane = threadIdx.x % kWave;
   const int wave = wave_id();
-  // PERSIST (the 8-row launch): one workgroup per CU stages the activation rows once and its
-  // waves then take groups of RPW weight rows in turn, group g by wave g mod (waves of the
-  // grid), numbered so that consecutive groups fall on different workgroups.  Every row is
-  // still computed by one wave with the operations of m = 1.
+  // PERSIST: the resident workgroups stage their activation rows once and then loop over
+  // units of weight rows.  With whole rows per wave (SPLIT == 1) a unit is one wave's RPW
+  // rows and unit g belongs to wave g mod (waves of the grid), the waves numbered so that
+  // consecutive units fall on different workgroups.  With rows split between waves a unit is
+  // the workgroup's ROWS rows, taken by the workgroups in turn, so that the waves sharing a
+  // row stay together.  Every row is still computed with the operations of m = 1.
   constexpr bool PERSIST = C::PERSIST;
-  static_assert(!PERSIST || SPLIT == 1, "a persistent wave owns whole rows");
-  const int ngroups = (out_f + RPW - 1) / RPW;
-  const int gstride = (int)gridDim.x * C::WAVES;
-  int grp = wave * (int)gridDim.x + (int)blockIdx.x;
-  int rbase = PERSIST ? grp * RPW : (blockIdx.x * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
+  const int nunits = SPLIT == 1 ? (out_f + RPW - 1) / RPW : (out_f + C::ROWS - 1) / C::ROWS;
+  const int ustride = SPLIT == 1 ? (int)gridDim.x * C::WAVES : (int)gridDim.x;
+  int unit = SPLIT == 1 && PERSIST ? wave * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x;
+  auto rbase_of = [&](int u) {
+    return SPLIT == 1 && PERSIST ? u * RPW : (u * (C::WAVES / SPLIT) + wave / SPLIT) * RPW;
+  };
+  int rbase = rbase_of(unit);
   const int part = wave % SPLIT;
   const int wbeg = part * nwin / SPLIT, wend = (part + 1) * nwin / SPLIT;  // this wave's windows
   const int nb = in_f / 32;
@@ -295,6 +299,7 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
       }
     }
   };
+  int pbuf = 0;  // SPLIT > 1: the partial-sum buffer of this unit
   for (;;) {
   if constexpr (C::DB) {
     int4_t wv2[U][RPW];
@@ -323,26 +328,18 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
           y[(int64_t)(t0 + tt) * out_f + rbase + r] = BLK ? s : s * scale;
       }
     }
-    if constexpr (!PERSIST) break;
-    // the next group of this wave, if any (wave-uniform)
-    grp += gstride;
-    if (grp >= ngroups) break;
-    rbase = grp * RPW;
-    setup_rows();
-    load(wv, gv1, wbeg);
-#pragma unroll
-    for (int tt = 0; tt < MT; ++tt)
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) acc[tt][r] = 0.0f;
   } else {
-    // the SPLIT partial sums of a row meet in LDS and are added in part order
-    __shared__ float psum[MT][C::WAVES * RPW];
+    // the SPLIT partial sums of a row meet in LDS and are added in part order; two buffers
+    // used in turn, because the barrier of the next unit is the first point where every wave
+    // has finished reading this one
+    __shared__ float psum[2][MT][C::WAVES * RPW];
+    float(*ps)[C::WAVES * RPW] = psum[pbuf];
 #pragma unroll
     for (int tt = 0; tt < MT; ++tt) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const float s = wave_sum(acc[tt][r]);
-        if (lane == 0) psum[tt][wave * RPW + r] = s;
+        if (lane == 0) ps[tt][wave * RPW + r] = s;
       }
     }
     __syncthreads();
@@ -351,15 +348,28 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         if (lane == 0 && part == 0 && rok[r] && t0 + tt < m) {
-          float s = psum[tt][wave * RPW + r];
+          float s = ps[tt][wave * RPW + r];
 #pragma unroll
-          for (int p = 1; p < SPLIT; ++p) s += psum[tt][(wave + p) * RPW + r];
+          for (int p = 1; p < SPLIT; ++p) s += ps[tt][(wave + p) * RPW + r];
           y[(int64_t)(t0 + tt) * out_f + rbase + r] = BLK ? s : s * scale;
         }
       }
     }
-    break;
+    pbuf ^= 1;
   }
+    if constexpr (!PERSIST) break;
+    // the next unit of this wave (SPLIT == 1) or workgroup (SPLIT > 1), if any: uniform over
+    // the wave, and over the workgroup when its waves share rows, so every wave of a
+    // workgroup meets the same barriers
+    unit += ustride;
+    if (unit >= nunits) break;
+    rbase = rbase_of(unit);
+    setup_rows();
+    load(wv, gv1, wbeg);
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) acc[tt][r] = 0.0f;
   }
 }
 
@@ -368,8 +378,9 @@ void k_gemv_e4m3(const uint8_t *__restrict__ W, int64_t row_bytes, float scale,
 template <class C>
 unsigned grid_x_for(int out_f, int in_f) {
   if constexpr (C::PERSIST) {
-    const int groups = (out_f + C::RPW - 1) / C::RPW;
-    const int want = (groups + C::WAVES - 1) / C::WAVES;
+    // units: groups of RPW rows (whole rows per wave) or of ROWS rows (rows split over waves)
+    const int want = C::SPLIT == 1 ? ((out_f + C::RPW - 1) / C::RPW + C::WAVES - 1) / C::WAVES
+                                   : (out_f + C::ROWS - 1) / C::ROWS;
     const int cap = cu_count() * C::wgs_per_cu(in_f);
     return (unsigned)(want < cap ? want : cap);
   } else {
@@ -383,9 +394,12 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
                       int in_f, int out_f, hipStream_t s) {
   auto kern = k_gemv_e4m3<BLK, C>;
   static std::atomic<bool> lds_set[kMaxDevices];
+  // The dynamic LDS limit leaves room for the kernel's static partial-sum buffers (at most
+  // 2 * MT * WAVES * RPW floats), which count against the same 160 KiB.
   const size_t want = C::MT * act_lds_bytes(C::MAX_IN_F) + kSinkBytes;
+  const size_t cap = kLdsBytes - 2 * C::MT * C::WAVES * C::RPW * sizeof(float);
   const hipError_t e = set_lds_limit_once(reinterpret_cast<const void *>(kern),
-                                          want < kLdsBytes ? want : kLdsBytes, lds_set);
+                                          want < cap ? want : cap, lds_set);
   if (e != hipSuccess) return e;
   const dim3 g(grid_x_for<C>(out_f, in_f), (m + C::MT - 1) / C::MT);
   hipLaunchKernelGGL(kern, g, dim3(C::THREADS), C::MT * act_lds_bytes(in_f) + kSinkBytes, s, W,
@@ -407,11 +421,13 @@ using CfgSmallB2 = Cfg<8, 1, 2, 1, 1, true, 8, 1, 2>;     //               m = 2
 using CfgSmallB4 = Cfg<8, 2, 1, 1, 1, true, 5, 1, 4>;     //               m = 3..4
 using CfgSmallB8 = Cfg<16, 2, 1, 1, 1, true, 4, 1, 8>;    //               m >= 5
 using CfgMid = Cfg<8, 1, 3, 3, 2, true, 8, 2>;            // in_f <= 24576, m = 1
-using CfgMidB2 = Cfg<8, 1, 3, 3, 2, true, 8, 2, 2>;       //                m >= 2
+using CfgMidB2 = Cfg<8, 1, 3, 3, 2, true, 8, 2, 2>;       //                m = 2 (and beyond 18432)
+using CfgMidB4 = Cfg<8, 1, 3, 3, 2, true, 4, 2, 4>;       // in_f <= 18432, m >= 3
 using CfgLarge = Cfg<16, 1, 4, 4, 4, true>;               // in_f <= 65536
 static_assert(CfgSmall::MAX_IN_F == 8192 && CfgSmallB2::MAX_IN_F >= 8192 &&
                   CfgSmallB4::MAX_IN_F >= 8192 && CfgSmallB8::MAX_IN_F >= 8192 &&
                   CfgMid::MAX_IN_F >= 24576 && CfgMidB2::MAX_IN_F >= 24576 &&
+                  CfgMidB4::MAX_IN_F >= 18432 &&
                   CfgLarge::MAX_IN_F == kMaxInF, "activation coverage");
 static_assert(CfgSmall::KD * CfgSmall::THREADS * 32 >= CfgSmall::MAX_IN_F &&
                   CfgSmallB2::KD * CfgSmallB2::THREADS * 32 >= 8192 &&
@@ -419,14 +435,19 @@ static_assert(CfgSmall::KD * CfgSmall::THREADS * 32 >= CfgSmall::MAX_IN_F &&
                   CfgSmallB8::KD * CfgSmallB8::THREADS * 32 >= 8192 &&
                   CfgMid::KD * CfgMid::THREADS * 32 >= CfgMid::MAX_IN_F &&
                   CfgMidB2::KD * CfgMidB2::THREADS * 32 >= 24576 &&
+                  CfgMidB4::KD * CfgMidB4::THREADS * 32 >= 18432 &&
                   CfgLarge::KD * CfgLarge::THREADS * 32 >= CfgLarge::MAX_IN_F,
               "scale coverage");
 static_assert(CfgSmallB8::MT * act_lds_bytes(8192) + kSinkBytes <= kLdsBytes &&
                   CfgMidB2::MT * act_lds_bytes(24576) + kSinkBytes <= kLdsBytes &&
+                  CfgMidB4::MT * act_lds_bytes(18432) + kSinkBytes +
+                          2 * CfgMidB4::MT * CfgMidB4::WAVES * CfgMidB4::RPW * sizeof(float) <=
+                      kLdsBytes &&
                   act_lds_bytes(kMaxInF) + kSinkBytes <= kLdsBytes,
               "staged rows fit the LDS of a workgroup");
 static_assert(CfgSmall::SPLIT == CfgSmallB2::SPLIT && CfgSmall::SPLIT == CfgSmallB4::SPLIT &&
-                  CfgSmall::SPLIT == CfgSmallB8::SPLIT && CfgMid::SPLIT == CfgMidB2::SPLIT,
+                  CfgSmall::SPLIT == CfgSmallB8::SPLIT && CfgMid::SPLIT == CfgMidB2::SPLIT &&
+                  CfgMid::SPLIT == CfgMidB4::SPLIT,
               "one row split per in_f range");
 
 // The launch shape for (m, in_f): f is called with the Tag of the chosen configuration.
@@ -438,7 +459,11 @@ auto with_cfg(int m, int in_f, F &&f) {
     if (m <= 4) return f(Tag<CfgSmallB4>{});
     return f(Tag<CfgSmallB8>{});
   }
-  if (in_f <= 24576) return m == 1 ? f(Tag<CfgMid>{}) : f(Tag<CfgMidB2>{});
+  if (in_f <= 24576) {
+    if (m == 1) return f(Tag<CfgMid>{});
+    if (m >= 3 && in_f <= 18432) return f(Tag<CfgMidB4>{});
+    return f(Tag<CfgMidB2>{});
+  }
   return f(Tag<CfgLarge>{});
 }
 
