@@ -509,12 +509,13 @@ using QSmallB2 = QCfg<4, 1, 3, 1, 2, true, 8, 1, 2>;      //               m = 2
 using QSmallB4 = QCfg<4, 1, 2, 1, 2, true, 5, 1, 4>;      //               m = 3..4
 using QSmallB8 = QCfg<8, 2, 1, 1, 3, true, 4, 1, 8>;      //               m >= 5
 using QMid = QCfg<4, 1, 4, 3, 4, true>;                   // in_f <= 24576, m = 1
-using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 1, 2>;        //                m >= 2
+using QMidB2 = QCfg<8, 1, 3, 2, 3, true, 8, 1, 2>;        //                m = 2
+using QMidB4 = QCfg<8, 1, 3, 2, 3, true, 4, 1, 4>;        //                m >= 3
 using QLarge = QCfg<16, 1, 4, 2, 3, true>;                // in_f <= 65536
 static_assert(QSmall::MAX_IN_F >= 8192 && QSmallB2::MAX_IN_F >= 8192 &&
                   QSmallB4::MAX_IN_F >= 8192 && QSmallB8::MAX_IN_F >= 8192 &&
                   QMid::MAX_IN_F >= 24576 && QMidB2::MAX_IN_F >= 24576 &&
-                  QLarge::MAX_IN_F == kMaxInF,
+                  QMidB4::MAX_IN_F >= 24576 && QLarge::MAX_IN_F == kMaxInF,
               "activation coverage of the in_f ranges dispatched to each shape");
 static_assert(QSmall::KD * QSmall::THREADS >= (int)dsc_entries(QSmall::MAX_IN_F) &&
                   QSmallB2::KD * QSmallB2::THREADS >= (int)dsc_entries(8192) &&
@@ -522,14 +523,17 @@ static_assert(QSmall::KD * QSmall::THREADS >= (int)dsc_entries(QSmall::MAX_IN_F)
                   QSmallB8::KD * QSmallB8::THREADS >= (int)dsc_entries(8192) &&
                   QMid::KD * QMid::THREADS >= (int)dsc_entries(QMid::MAX_IN_F) &&
                   QMidB2::KD * QMidB2::THREADS >= (int)dsc_entries(24576) &&
+                  QMidB4::KD * QMidB4::THREADS >= (int)dsc_entries(24576) &&
                   QLarge::KD * QLarge::THREADS >= (int)dsc_entries(QLarge::MAX_IN_F),
               "scale coverage");
 static_assert(fast_lds_bytes(8192, QSmallB8::MT) <= kLdsBytes &&
                   fast_lds_bytes(24576, QMidB2::MT) <= kLdsBytes &&
+                  fast_lds_bytes(24576, QMidB4::MT) <= kLdsBytes &&
                   fast_lds_bytes(kMaxInF, 1) <= kLdsBytes,
               "staged rows fit the LDS of a workgroup");
 static_assert(QSmall::SPLIT == QSmallB2::SPLIT && QSmall::SPLIT == QSmallB4::SPLIT &&
-                  QSmall::SPLIT == QSmallB8::SPLIT && QMid::SPLIT == QMidB2::SPLIT,
+                  QSmall::SPLIT == QSmallB8::SPLIT && QMid::SPLIT == QMidB2::SPLIT &&
+                  QMid::SPLIT == QMidB4::SPLIT,
               "one row split per in_f range");
 
 }  // namespace
@@ -545,7 +549,11 @@ auto with_cfg(int m, int in_f, F &&f) {
     if (m <= 4) return f(Tag<QSmallB4>{});
     return f(Tag<QSmallB8>{});
   }
-  if (in_f <= 24576) return m == 1 ? f(Tag<QMid>{}) : f(Tag<QMidB2>{});
+  if (in_f <= 24576) {
+    if (m == 1) return f(Tag<QMid>{});
+    if (m == 2) return f(Tag<QMidB2>{});
+    return f(Tag<QMidB4>{});
+  }
   return f(Tag<QLarge>{});
 }
 
