@@ -36,9 +36,10 @@
 // each weight chunk is decoded once and multiplied into every row with the same operations
 // in the same order as for MT = 1, and every launch shape of an in_f range splits rows the
 // same way, so row t of an m-row call is bit-identical to an m=1 call on that row.  The
-// launches for 3-8 rows of up to 8192 columns are persistent: as many workgroups as fit on the
-// device stage their activation rows once, and each wave then takes groups of RPW weight rows
-// in turn, so that the staging is not repeated per row group and the last groups spread over
+// launches for 3 or more rows of up to 18432 columns are persistent: as many workgroups as fit
+// on the device stage their activation rows once and then loop over the weight rows (each
+// wave over groups of RPW rows, or, where two waves share a row, each workgroup over blocks
+// of rows), so that the staging is not repeated per row group and the last groups spread over
 // all CUs instead of leaving a partial round of workgroups.
 #include "common.hpp"
 
@@ -413,7 +414,8 @@ hipError_t launch_cfg(const uint8_t *W, int64_t row_bytes, float scale, const fl
 // flight; 6% faster at 5120 x 17408); 16 waves beyond.  All double-buffer their windows
 // (2 to 4 per batch) and fit 64 VGPRs.
 // Several activation rows (m > 1) share each weight pass: up to 8 rows per workgroup for
-// in_f <= 8192, 2 up to 24576 and 1 beyond (LDS holds one staged row per activation row).  Every shape
+// in_f <= 8192, 4 up to 18432, 2 up to 24576 and 1 beyond (LDS holds one staged row per
+// activation row).  Every shape
 // used for one in_f range splits rows the same way (SPLIT), so each activation row is
 // computed in the same order whatever m is.
 using CfgSmall = Cfg<4, 1, 2, 2, 1, true>;                // in_f <= 8192, m = 1

@@ -42,8 +42,8 @@
 // multiplies it by its own d_a there; that is the product the scale's own lane forms for
 // MT = 1, so the bits are the same.)  Every launch shape
 // of an in_f range splits rows the same way, so each activation row of an m-row call is
-// bit-identical to an m=1 call on that row.  The launches for 3-8 rows of up to 8192 columns
-// are persistent, as in the e4m3 stream: the device's resident workgroups stage their
+// bit-identical to an m=1 call on that row.  The launches for 3 or more rows of up to 24576
+// columns are persistent, as in the e4m3 stream: the device's resident workgroups stage their
 // activation rows once and their waves take groups of RPW weight rows in turn.
 #include "common.hpp"
 

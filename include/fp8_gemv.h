@@ -332,7 +332,8 @@ int fp8gemv_read_pattern(const void *p, int64_t bytes, int pattern, int64_t row_
  *   info        out: grid in workgroups (x = weight rows, y = activation-row passes), threads per
  *               workgroup, dynamic LDS bytes, the kernel family and its launch configuration as
  *               they appear in the demangled kernel symbol (static strings).  The launches for
- *               3-8 activation rows of up to 8192 columns are persistent: their grid_x is the
+ *               3 or more activation rows on the vector kernels (rows of up to 18432 columns
+ *               for e4m3, 24576 for Q8_0) are persistent: their grid_x is the
  *               workgroups that fit on the current device at once (its CU count, read once per
  *               device; 256 CUs are assumed where it cannot be read), whose waves loop over the
  *               weight rows.
