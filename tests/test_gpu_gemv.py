@@ -448,10 +448,10 @@ def test_graph_replays_match_eager(fg):
 
 
 def test_graph_replays_of_the_other_entry_points(fg):
-    # The two-launch chains, the SiLU-gated producer, m = 4 rows (plain and matrix-core
-    # entry points) and the requantiser under graph replay: every replay, with eager work
+    # The two-launch chains, the SiLU-gated and KDA gated-norm producers, m = 4 rows (plain and
+    # matrix-core entry points) and the requantiser under graph replay: every replay, with eager work
     # between replays, reproduces the eager bytes.
-    case("graph replay of chains, silu producer, m = 4 and requant")
+    case("graph replay of chains, silu and gated producers, m = 4 and requant")
     in_f, out_f = 2048, 384
     x = to_dev(synth.x_rows(in_f, 4))
     w = to_dev(synth.gain(in_f))
@@ -462,18 +462,23 @@ def test_graph_replays_of_the_other_entry_points(fg):
     h = torch.empty(in_f, device=dev())
     hq = torch.empty(in_f, dtype=torch.int8, device=dev())
     hd = torch.empty(in_f // 32, device=dev())
+    go, gg, gw = to_dev(synth.f32(7, in_f)), to_dev(synth.f32(8, in_f)), to_dev(synth.gain(128))
+    gz = torch.empty(in_f, device=dev())
+    gq = torch.empty(in_f, dtype=torch.int8, device=dev())
+    gdd = torch.empty(in_f // 32, device=dev())
     c = Case("blk128", out_f, in_f, 1)
     y = torch.empty((4, out_f), device=dev())
     Wq = torch.empty(out_f * in_f // 32 * 34, dtype=torch.uint8, device=dev())
     yq = torch.empty((4, out_f), device=dev())
     ymc = torch.empty((4, out_f), device=dev())
     yqmc = torch.empty((4, out_f), device=dev())
-    outs = [z, qs, d, h, hq, hd, y, Wq, yq, ymc, yqmc]
+    outs = [z, qs, d, h, hq, hd, gz, gq, gdd, y, Wq, yq, ymc, yqmc]
 
     def run():
         fg.rms_norm_f32(x, w, z, in_f, 4)
         fg.quantize_q8_1(z, qs, d, 4, in_f)
         fg.silu_mul_q8_1(gate, up, h, hq, hd, in_f, 1)
+        fg.gated_rmsnorm_q8_1(go, gg, gw, gz, gq, gdd, in_f, 128, 1)
         fg.gemv_e4m3_blk128_q81(c.Wd, c.row_bytes, c.gd, c.grid.shape[1], qs, d, y, 4, in_f,
                                 out_f)
         fg.requant_e4m3_blk128_q8_0(c.Wd, c.row_bytes, c.gd, c.grid.shape[1], Wq,
