@@ -57,6 +57,9 @@ MUTANTS = [
     # SiLU-gated product
     ("silu sign of the exponent", "oracle.c", "g / (1.0 + exp(-g))", "g / (1.0 + exp(g))", 0),
     ("silu as a plain sigmoid", "oracle.c", "g / (1.0 + exp(-g))", "1.0 / (1.0 + exp(-g))", 0),
+    ("silu up factor dropped", "oracle.c", "double h = sg * (double)up[i];", "double h = sg;", 0),
+    ("silu rounded to f32 before the product", "oracle.c", "double h = sg * (double)up[i];",
+     "double h = (double)(float)sg * (double)up[i];", 0),
     # RMSNorm and the KDA gated norm (Python, f64)
     ("rmsnorm eps dropped", "__init__.py", "math.sqrt(ss / ncols + eps64)", "math.sqrt(ss / ncols)", 0),
     ("rmsnorm divides by n - 1", "__init__.py", "math.sqrt(ss / ncols + eps64)", "math.sqrt(ss / (ncols - 1) + eps64)", 0),
